@@ -1,0 +1,18 @@
+"""Exact IO-aware attention for MI355X (gfx950).
+
+The compute path is the C-ABI library ``libmiattn.so`` (hand-written HIP
+kernels); this package is its thin Python binding plus the seeded synthetic
+inputs and the work accounting used by the tests and the benchmark.
+"""
+from . import accounting, inputs  # noqa: F401
+
+_BINDING_NAMES = ("attn_fwd", "attn_decode", "attn_fwd_workspace_bytes",
+                  "attn_decode_workspace_bytes", "attn_status_str", "library",
+                  "MiattnError")
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,42 @@
+"""Plain fp64 CPU oracle for exact scaled dot-product attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute anything in this package: only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` use it. It shares no code with the
+HIP library or its Python binding, and imports neither.
+
+What it computes (each function cites the page passage it follows):
+
+* ``attention``      -- softmax(scale * Q K^T) V, materialising S and P in fp64,
+                        with causal / block / key-length masks and GQA heads.
+* ``decode``         -- one new query per sequence against a KV cache.
+* ``logit_bound``    -- the Cauchy-Schwarz upper bound on each row's logits
+                        (optionally with mean-centred keys).
+* ``fixed_max_eligible`` -- the per-row-group eligibility rule for that bound.
+* ``fixed_max_attention`` -- softmax evaluated against the bound instead of the
+                        row maximum (equal to ``attention`` in exact arithmetic).
+* ``online_softmax``  -- the running (max, sum) recurrence over blocks of a row.
+* ``merge_partials``  -- combining (O, LSE) pairs of disjoint key sets.
+
+Pins (tests/test_oracle.py): printed worked examples (tests/golden/), closed
+forms (single key, identical keys, causal first row), invariants (row sums,
+joint permutation, shift invariance, split == unsplit), library routines
+(torch SDPA in float64 on the CPU, scipy logsumexp) and an independent
+frame-gather construction for block masks.
+
+Parity unpinned: the eligibility threshold ``TAU`` = 64 is a constant chosen
+here from an underflow argument, not a value the pages give; only the rule's
+soundness (the normaliser stays far above the fp32 minimum) is tested.
+"""
+
+from .attention import (  # noqa: F401
+    TAU,
+    attention,
+    decode,
+    element_mask,
+    fixed_max_attention,
+    fixed_max_eligible,
+    logit_bound,
+    merge_partials,
+    online_softmax,
+)

@@ -1,0 +1,281 @@
+"""fp64 reference attention, written out from its definition.
+
+Pages cited (by title and section):
+
+* "Attention Mechanism Optimization for Efficient LLM Inference"
+  (pyy0715.github.io): "Background: Scaled Dot-Product Attention" (the formula),
+  "Multi-Query Attention (MQA) / Comparison" (the [batch, seq, h, d_k] layout),
+  "Grouped-Query Attention (GQA)" (the head-group diagram), "Role of KV Cache"
+  and "Two Phases of Inference / Decode" (one new query against the cache),
+  "FlashAttention / Tiling" (the softmax row sum), "Online-Softmax" (the
+  running max / running sum recurrence and its worked example).
+* "플래시어텐션: 메모리를 아끼는 정확한 어텐션" (FlashAttention explainer, base.kaita.kr):
+  §2 타일링 (block max m and sum l, rescaled by exp(m_block - m_total)),
+  §3 알고리즘 (Theorem 1: the tiled result is exactly softmax(QK^T)V),
+  §4 재계산 (only O and the statistics (m, l) are kept), §6 블록 희소 (zero
+  blocks of the block mask are not computed).
+* "TPU attention 최적화 실전 가이드" (aibase.it): 3단계 (frame-aligned blocks, no
+  partial blocks), 4단계 (logit upper bound from the query norm and the largest
+  key norm; mean-centred keys; per-head eligibility with fallback).
+
+Everything is float64 NumPy. S and P are materialised per (batch, head) in row
+chunks; rows are independent, so chunking changes nothing.
+"""
+
+import numpy as np
+
+# Eligibility threshold for the fixed-max softmax, in nats. Parity unpinned:
+# chosen here, not given by the pages (see fixed_max_eligible).
+TAU = 64.0
+
+_ROW_CHUNK = 2048
+
+
+def _check_heads(hq, hkv):
+    if hkv <= 0 or hq % hkv != 0:
+        raise ValueError(f"query heads ({hq}) must be a multiple of KV heads ({hkv})")
+    return hq // hkv
+
+
+def element_mask(nq, nk, *, causal=False, block_mask=None, block_q=None,
+                 block_k=None, kv_len=None, rows=None):
+    """Boolean [len(rows), nk] mask of allowed (query i, key j) pairs.
+
+    Each rule is ANDed in, element by element:
+
+    * causal: key j is visible to query i iff j <= i + (nk - nq). With nq == nk
+      this is j <= i; with nq == 1 the single query sees every key, as a new
+      token sees the whole cache ("Two Phases of Inference / Decode").
+    * block: block_mask[i // block_q, j // block_k] != 0; a zero block is not
+      computed (FlashAttention explainer §6 블록 희소).
+    * kv_len: j < kv_len (the keys that exist in the cache).
+    """
+    if rows is None:
+        rows = np.arange(nq)
+    rows = np.asarray(rows)
+    cols = np.arange(nk)
+    allowed = np.ones((rows.size, nk), dtype=bool)
+    if causal:
+        allowed &= cols[None, :] <= rows[:, None] + (nk - nq)
+    if block_mask is not None:
+        bm = np.asarray(block_mask)
+        allowed &= bm[(rows // block_q)[:, None], (cols // block_k)[None, :]] != 0
+    if kv_len is not None:
+        allowed &= cols[None, :] < int(kv_len)
+    return allowed
+
+
+def attention(q, k, v, scale, *, causal=False, block_mask=None, block_q=None,
+              block_k=None, kv_len=None, heads=None, rows=None):
+    """Exact attention O = softmax(scale * Q K^T) V and per-row LSE.
+
+    q: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d] (any float dtype; computed in fp64).
+    kv_len: optional [B] ints, keys j >= kv_len[b] are excluded.
+    heads / rows: optional subsets of query heads / query rows to evaluate
+    (for sampling large problems); the result then has those extents.
+
+    Returns (O [B, len(rows), len(heads), d] fp64, LSE [B, len(heads), len(rows)]).
+
+    Steps, per batch b and query head h:
+    1. GQA: query head h reads KV head h // (Hq / Hkv) -- contiguous groups, as
+       in the GQA diagram where with 2 KV groups Q1..Q4 use KV1 and Q5..Q8 use
+       KV2 ("Grouped-Query Attention (GQA)"); Hkv == 1 is MQA, Hkv == Hq is MHA.
+    2. S = scale * Q K^T, materialised ("Background: Scaled Dot-Product
+       Attention"; scale = 1/sqrt(d_k) there, an explicit argument here).
+    3. Disallowed pairs get -inf, so they contribute exactly 0 below.
+    4. m = row max of S; P = exp(S - m); l = row sum of P; P = P / l
+       (the safe softmax of "FlashAttention / Tiling" and "Online-Softmax").
+    5. O = P V; LSE = m + ln l (natural log of the row's normaliser over the
+       scaled scores, the statistic kept for the backward pass, FlashAttention
+       explainer §4 재계산).
+    A row with no allowed key returns O = 0 and LSE = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Nq, Hq, d = q.shape
+    Bk, Nk, Hkv, dk = k.shape
+    if Bk != B or dk != d or v.shape != k.shape:
+        raise ValueError("q/k/v shapes do not agree")
+    group = _check_heads(Hq, Hkv)
+    heads = np.arange(Hq) if heads is None else np.asarray(heads)
+    rows = np.arange(Nq) if rows is None else np.asarray(rows)
+
+    O = np.zeros((B, rows.size, heads.size, d), dtype=np.float64)
+    LSE = np.full((B, heads.size, rows.size), -np.inf, dtype=np.float64)
+    for b in range(B):
+        klen = None if kv_len is None else int(kv_len[b])
+        for hi, h in enumerate(heads):
+            kvh = h // group
+            Kb = k[b, :, kvh, :]
+            Vb = v[b, :, kvh, :]
+            for r0 in range(0, rows.size, _ROW_CHUNK):
+                rr = rows[r0:r0 + _ROW_CHUNK]
+                S = scale * (q[b, rr, h, :] @ Kb.T)
+                allowed = element_mask(Nq, Nk, causal=causal, block_mask=block_mask,
+                                       block_q=block_q, block_k=block_k,
+                                       kv_len=klen, rows=rr)
+                S = np.where(allowed, S, -np.inf)
+                m = S.max(axis=1)
+                live = allowed.any(axis=1)
+                m_safe = np.where(live, m, 0.0)
+                P = np.exp(S - m_safe[:, None])
+                P = np.where(allowed, P, 0.0)
+                l = P.sum(axis=1)
+                l_safe = np.where(live, l, 1.0)
+                Pn = P / l_safe[:, None]
+                O[b, r0:r0 + rr.size, hi, :] = np.where(live[:, None], Pn @ Vb, 0.0)
+                LSE[b, hi, r0:r0 + rr.size] = np.where(live, m_safe + np.log(l_safe), -np.inf)
+    return O, LSE
+
+
+def decode(q, k_cache, v_cache, seqlens, scale, heads=None):
+    """One query token per sequence against a contiguous KV cache.
+
+    q: [B, Hq, d]; k_cache, v_cache: [B, max_len, Hkv, d]; seqlens: [B] ints in
+    [0, max_len]. The new query attends to every cached key of its sequence and
+    nothing past the sequence's length ("Role of KV Cache"; "Two Phases of
+    Inference / Decode": Q_new against the cache K_1..K_t). This is attention
+    with Nq = 1, no causal rule, and keys limited to seqlens[b].
+
+    Returns (O [B, Hq', d], LSE [B, Hq']).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    O, LSE = attention(q[:, None, :, :], k_cache, v_cache, scale,
+                       kv_len=np.asarray(seqlens), heads=heads)
+    return O[:, 0, :, :], LSE[:, :, 0]
+
+
+def logit_bound(q, k, scale, *, centered=False):
+    """Upper bound M[b, h, i] on every logit scale * q_i . k_j of a row.
+
+    TPU attention guide, 4단계: by Cauchy-Schwarz, q . k <= |q| |k| <= |q| max_j |k_j|,
+    so M_i = scale * |q_i| * max_j |k_j| bounds the row before any key block
+    is seen. The max runs over all Nk keys of the (batch, KV head).
+
+    centered=True uses the mean key kbar and R = max_j |k_j - kbar|:
+    q . k_j = q . kbar + q . (k_j - kbar) <= q . kbar + |q| R, so
+    M_i = scale * (q_i . kbar + |q_i| R) also bounds the raw logits (the guide
+    notes centring can tighten the bound and leaves softmax unchanged).
+    Assumes scale > 0.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    group = _check_heads(Hq, Hkv)
+    M = np.empty((B, Hq, Nq), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            K = k[b, :, h // group, :]
+            Q = q[b, :, h, :]
+            qn = np.sqrt((Q * Q).sum(axis=1))
+            if not centered:
+                kmax = np.sqrt((K * K).sum(axis=1)).max()
+                M[b, h] = scale * qn * kmax
+            else:
+                kbar = K.mean(axis=0)
+                R = np.sqrt(((K - kbar) ** 2).sum(axis=1)).max()
+                M[b, h] = scale * (Q @ kbar + qn * R)
+    return M
+
+
+def fixed_max_eligible(qnorm_rows, rho, scale, tau=TAU):
+    """Eligibility of a group of query rows for the fixed-max softmax.
+
+    TPU attention guide, 4단계: a bound far above the true row max pushes the
+    exponentials toward underflow, so each group is checked and falls back to
+    the running-max softmax when the bound is loose. Every logit of row i lies
+    in [M_i - 2 * scale * |q_i| * rho, M_i], where rho = max_j |k_j| for the
+    plain bound and max_j |k_j - kbar| for the centred one (Cauchy-Schwarz from
+    both sides). So the row's largest term exp(s_max - M_i) is at least
+    exp(-2 * scale * |q_i| * rho). Rule: eligible iff
+    2 * scale * max_i |q_i| * rho <= tau; then every row normaliser is at least
+    exp(-tau), far above the float32 minimum normal exp(-87.3).
+
+    Parity unpinned: tau (default 64 nats) is chosen here.
+    """
+    qn = np.asarray(qnorm_rows, dtype=np.float64)
+    return bool(2.0 * scale * qn.max() * float(rho) <= tau)
+
+
+def fixed_max_attention(q, k, v, scale, M, *, causal=False, block_mask=None,
+                        block_q=None, block_k=None):
+    """Softmax evaluated against a fixed per-row reference M instead of the max.
+
+    P_ij = exp(S_ij - M_i) / sum_t exp(S_it - M_i). Multiplying numerator and
+    denominator by exp(M_i - m_i) shows this equals the max-subtracted softmax
+    exactly (the shift invariance the TPU guide's 4단계 relies on). LSE = M + ln l.
+    M: [B, Hq, Nq].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    group = _check_heads(Hq, Hkv)
+    O = np.zeros((B, Nq, Hq, d))
+    LSE = np.full((B, Hq, Nq), -np.inf)
+    allowed = element_mask(Nq, Nk, causal=causal, block_mask=block_mask,
+                           block_q=block_q, block_k=block_k)
+    for b in range(B):
+        for h in range(Hq):
+            S = scale * (q[b, :, h, :] @ k[b, :, h // group, :].T)
+            E = np.where(allowed, np.exp(S - M[b, h][:, None]), 0.0)
+            l = E.sum(axis=1)
+            live = l > 0
+            ls = np.where(live, l, 1.0)
+            O[b, :, h, :] = np.where(live[:, None], (E / ls[:, None]) @ v[b, :, h // group, :], 0.0)
+            LSE[b, h] = np.where(live, M[b, h] + np.log(ls), -np.inf)
+    return O, LSE
+
+
+def online_softmax(x, block_sizes):
+    """Running (max, sum) over a row read block by block.
+
+    "Online-Softmax" (LLM inference page): for each new block B_new,
+    m_new = max(m_old, max(B_new)) and
+    d_new = d_old * exp(m_old - m_new) + sum(exp(B_new - m_new)).
+    Returns the list of (m, d) after each block; the last pair gives the row's
+    normaliser Z = exp(m) * d.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if sum(block_sizes) != x.size:
+        raise ValueError("blocks must cover the row")
+    m, dsum = -np.inf, 0.0
+    out = []
+    pos = 0
+    for n in block_sizes:
+        blk = x[pos:pos + n]
+        pos += n
+        m_new = max(m, blk.max())
+        dsum = dsum * np.exp(m - m_new) + np.exp(blk - m_new).sum()
+        m = m_new
+        out.append((m, dsum))
+    return out
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combine results computed over disjoint key sets.
+
+    FlashAttention explainer §2 타일링: with a new overall max, each block's sum
+    (and its output) is rescaled by exp(m_block - m_total) and added. With each
+    part carrying its normalised output O_c and LSE_c = m_c + ln l_c, that is
+    LSE = max_c LSE_c + ln sum_c exp(LSE_c - max) and
+    O = sum_c exp(LSE_c - LSE) O_c. Parts with LSE_c = -inf contribute nothing;
+    if every part is empty, O = 0 and LSE = -inf.
+
+    o_parts: [C, ..., d]; lse_parts: [C, ...].
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    mx = lse_parts.max(axis=0)
+    live = np.isfinite(mx)
+    mx_safe = np.where(live, mx, 0.0)
+    w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - mx_safe), 0.0)
+    tot = w.sum(axis=0)
+    tot_safe = np.where(live, tot, 1.0)
+    lse = np.where(live, mx_safe + np.log(tot_safe), -np.inf)
+    o = (w[..., None] * o_parts).sum(axis=0) / tot_safe[..., None]
+    o = np.where(live[..., None], o, 0.0)
+    return o, lse
