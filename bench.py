@@ -1,0 +1,210 @@
+"""Benchmark of the hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over synthetic inputs already
+resident in HBM: a causal GQA prefill (attn_fwd, Llama-3-8B shape:
+B=1, Hq=32, Hkv=8, N=8192, d=128, bf16) followed by a GQA split-K decode
+(attn_decode, B=64, Hq=32, Hkv=8, d=128, bf16 cache of 32768 rows, lengths
+uniform in [1024, 32768]). Each part is timed with HIP events on the stream
+the library launches on (torch's current stream).
+
+Printed (one JSON line):
+  value      prefill forward throughput, TFLOP/s of algorithmic work
+             (4 d per attended query-key pair) over the prefill part of the steps
+  decode     KV-read GB/s of the decode part (sum of lengths x Hkv x d x 2 x 2 B)
+  roofline   prefill kernel against the dense bf16 MFMA peak
+  roofline_decode  decode against the HBM peak
+  cpu_baseline  the fp64 oracle on the host cores, on a bounded sample
+
+--workload runs a single named workload instead (one call per step):
+gpt2-causal, llama3-8b-gqa-causal-8k, gqa-decode-b64, video-frames-16x880
+(online), video-frames-16x880-fixed, video-frames-16x880-centered, tiny-f32.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK = 2516.6   # TFLOP/s, 256 CU x 4096 FLOP/clk x 2.4 GHz (dense)
+FP32_PEAK = 157.3         # TFLOP/s
+HBM_PEAK = 8000.0         # GB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="default")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+class Part:
+    """One call of a workload with pre-allocated inputs/outputs/workspace."""
+
+    def __init__(self, name, dev):
+        import torch
+        from exact_io_aware_attn_amd import accounting as acc
+        from exact_io_aware_attn_amd import binding as bd
+        from exact_io_aware_attn_amd.inputs import WORKLOADS, workload_inputs
+
+        base = name.replace("-fixed", "").replace("-centered", "")
+        self.softmax = "fixed_max" if name.endswith("-fixed") else (
+            "fixed_max_centered" if name.endswith("-centered") else "online")
+        self.name = name
+        self.w = w = WORKLOADS[base]
+        self.ins = ins = workload_inputs(w, device=dev)
+        self.kind = w.kind
+        if w.kind == "prefill":
+            q, k, v = ins["q"], ins["k"], ins["v"]
+            self.o = torch.empty_like(q)
+            self.lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+            bm = ins.get("block_mask")
+            self.bm = None if bm is None else torch.from_numpy(bm).to(dev)
+            mode = bd.SOFTMAX_MODES[self.softmax]
+            need = bd.attn_fwd_workspace_bytes(w.B, w.Hkv, w.Nk, w.d, mode)
+            self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
+            self.flops, self.bytes = acc.workload_work(w, block_mask=bm)
+            self.call = lambda: bd.attn_fwd(
+                q, k, v, causal=w.causal, block_mask=self.bm,
+                block=(w.block, w.block) if self.bm is not None else None,
+                softmax=self.softmax, out=self.o, lse_out=self.lse, workspace=self.ws)
+        else:
+            sl = ins["seqlens"]
+            self.o = torch.empty_like(ins["q"])
+            self.lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+            need = bd.attn_decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nk, w.d, 0)
+            self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            self.seqlens_host = sl.cpu().numpy()
+            self.flops, self.bytes = acc.workload_work(w, seqlens=self.seqlens_host)
+            self.call = lambda: bd.attn_decode(ins["q"], ins["k_cache"], ins["v_cache"], sl,
+                                               out=self.o, lse_out=self.lse, workspace=self.ws)
+
+
+def cpu_baseline(part, budget_s):
+    """The oracle, as it is, on a bounded sample of the prefill workload: whole
+    query heads of batch 0, one at a time, until the time budget is spent."""
+    import numpy as np
+    import oracle
+    from exact_io_aware_attn_amd import accounting as acc
+
+    w = part.w
+    ins = part.ins
+    f64 = lambda t: t.to("cpu").double().numpy()
+    q, k, v = f64(ins["q"][:1]), f64(ins["k"][:1]), f64(ins["v"][:1])
+    bm = ins.get("block_mask")
+    kw = dict(causal=w.causal)
+    if bm is not None:
+        kw.update(block_mask=bm, block_q=w.block, block_k=w.block)
+    pairs = acc.attended_pairs(w.Nq, w.Nk, causal=w.causal, block_mask=bm,
+                               block_q=w.block or None, block_k=w.block or None)
+    heads = 0
+    t0 = time.perf_counter()
+    while heads < w.Hq and (heads == 0 or time.perf_counter() - t0 < budget_s):
+        oracle.attention(q, k, v, w.scale, heads=[heads], **kw)
+        heads += 1
+    dt = time.perf_counter() - t0
+    flops = 4 * w.d * pairs * heads
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    cores = threads or len(os.sched_getaffinity(0))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{w.name}: batch 0, {heads} of {w.Hq} query heads, all {w.Nq} rows "
+                      f"(fp64 NumPy, S and P materialised), {dt:.1f} s",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    if args.workload == "default":
+        names = ["llama3-8b-gqa-causal-8k", "gqa-decode-b64"]
+    else:
+        names = [args.workload]
+    parts = [Part(n, dev) for n in names]
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for p in parts:
+            p.call()
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in parts] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, p in enumerate(parts):
+            ev[s][i][0].record()
+            p.call()
+            ev[s][i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+          for i in range(len(parts))]
+    ms_avg = [sum(m) / len(m) for m in ms]
+    ms_step = wall * 1e3 / args.steps
+
+    main_p = parts[0]
+    out = {"metric": "fwd attn TFLOP/s & %MFMA peak (prefill); KV-read GB/s & %HBM peak (decode)"}
+    if main_p.kind == "prefill":
+        tflops = main_p.flops / (ms_avg[0] * 1e-3) / 1e12
+        peak = MFMA_BF16_PEAK if main_p.w.dtype == "bf16" else FP32_PEAK
+        out.update(value=tflops, unit="TFLOP/s")
+        roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                "frac": tflops / peak, "traffic": None}
+    else:
+        gbs = main_p.bytes / (ms_avg[0] * 1e-3) / 1e9
+        out.update(value=gbs, unit="GB/s")
+        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK, "traffic": None}
+    out.update(n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=ms_step,
+               higher_is_better=True, scaling="weak", vs_baseline=None,
+               dtype="bf16" if main_p.w.dtype == "bf16" else "f32",
+               data="synthetic (seeded N(0,1) inputs, generated on the GPU)")
+    cfg = {"workload": " + ".join(p.name for p in parts)}
+    for p in parts:
+        w = p.w
+        cfg[p.name] = {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                       "causal": w.causal, "softmax": p.softmax,
+                       "flops": p.flops, "bytes": p.bytes}
+    out["config"] = cfg
+    out["ms_parts"] = {p.name: m for p, m in zip(parts, ms_avg)}
+    out["roofline"] = roof
+    if len(parts) > 1 and parts[1].kind == "decode":
+        d = parts[1]
+        gbs = d.bytes / (ms_avg[1] * 1e-3) / 1e9
+        out["decode"] = {"value": gbs, "unit": "GB/s", "ms": ms_avg[1]}
+        out["roofline_decode"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK,
+                                  "unit": "GB/s", "frac": gbs / HBM_PEAK, "traffic": None}
+    if not args.no_cpu_baseline and main_p.kind == "prefill":
+        out["cpu_baseline"] = cpu_baseline(main_p, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,187 @@
+"""ctypes binding of libmiattn.so (the C ABI in include/miattn.h).
+
+Argument marshalling only: tensors become device pointers and element
+strides, outputs and the workspace are allocated with torch when the caller
+does not pass them, and the call is enqueued on torch's current stream. Every
+step of the computation runs in the library's HIP kernels. If the library is
+not built, or there is no GPU, the calls raise; there is no fallback.
+"""
+
+import ctypes
+import math
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmiattn.so")
+
+MIATTN_BF16, MIATTN_F32 = 0, 1
+MIATTN_MASK_NONE, MIATTN_MASK_CAUSAL, MIATTN_MASK_BLOCK = 0, 1, 2
+SOFTMAX_MODES = {"online": 0, "fixed_max": 1, "fixed_max_centered": 2}
+
+_EXPORTS = ("attn_fwd", "attn_fwd_workspace_bytes", "attn_decode",
+            "attn_decode_workspace_bytes", "attn_decode_chunk", "attn_status_str")
+
+
+class MiattnError(RuntimeError):
+    def __init__(self, status, fn):
+        self.status = int(status)
+        super().__init__(f"{fn} failed with status {status}: {attn_status_str(status)}")
+
+
+class _Strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("s", ctypes.c_int64), ("h", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def library():
+    """Load libmiattn.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m exact_io_aware_attn_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_status_str.argtypes = [I]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_fwd_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.attn_fwd_workspace_bytes.restype = Z
+    lib.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, I, I, I,
+                             ctypes.POINTER(_Strides), P, Z, P]
+    lib.attn_fwd.restype = I
+    lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.attn_decode_workspace_bytes.restype = Z
+    lib.attn_decode_chunk.argtypes = [I, I, I, I]
+    lib.attn_decode_chunk.restype = I
+    lib.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I,
+                                ctypes.POINTER(_Strides), P, Z, P]
+    lib.attn_decode.restype = I
+    _lib = lib
+    return lib
+
+
+def attn_status_str(status):
+    return library().attn_status_str(int(status)).decode()
+
+
+def attn_fwd_workspace_bytes(B, Hkv, Nk, d, softmax_mode):
+    return int(library().attn_fwd_workspace_bytes(B, Hkv, Nk, d, softmax_mode))
+
+
+def attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d, kv_chunk=0):
+    return int(library().attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d, kv_chunk))
+
+
+def attn_decode_chunk(B, Hkv, max_len, kv_chunk=0):
+    return int(library().attn_decode_chunk(B, Hkv, max_len, kv_chunk))
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return MIATTN_BF16
+    if t.dtype == torch.float32:
+        return MIATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check_gpu(*ts):
+    dev = ts[0].device
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if t.device != dev:
+            raise ValueError("tensors must be on one device")
+
+
+def _strides4(t):
+    sb, ss, sh, sd = t.stride()
+    if sd != 1 and t.shape[3] > 1:
+        raise ValueError("the last (head) dimension must be contiguous")
+    return _Strides(sb, ss, sh)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def attn_fwd(q, k, v, *, causal=False, block_mask=None, block=None, scale=None,
+             softmax="online", return_lse=True, out=None, lse_out=None, workspace=None):
+    """Exact attention of q [B,Nq,Hq,d] against k, v [B,Nk,Hkv,d] (GPU tensors,
+    bf16 or fp32). block_mask: uint8 [Nq/bq, Nk/bk] (GPU tensor or array),
+    block = (bq, bk). Returns (o, lse) with lse [B,Hq,Nq] fp32 (or None)."""
+    _check_gpu(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B,Nq,Hq,d]; k and v [B,Nk,Hkv,d]")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    dev = q.device
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    mode = SOFTMAX_MODES[softmax]
+    mask_kind = MIATTN_MASK_CAUSAL if causal else MIATTN_MASK_NONE
+    bm = None
+    bq = bk = 0
+    if block_mask is not None:
+        mask_kind |= MIATTN_MASK_BLOCK
+        bq, bk = block
+        if isinstance(block_mask, np.ndarray):
+            block_mask = torch.from_numpy(np.ascontiguousarray(block_mask, dtype=np.uint8))
+        bm = block_mask.to(device=dev, dtype=torch.uint8).contiguous()
+    o = torch.empty_like(q) if out is None else out
+    _check_gpu(o)
+    lse = None
+    if return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev) if lse_out is None else lse_out
+    need = attn_fwd_workspace_bytes(B, Hkv, Nk, d, mode)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = (_Strides * 4)(_strides4(q), _strides4(k), _strides4(v), _strides4(o))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dtype_code(q),
+                            B, Hq, Hkv, Nq, Nk, d, scale, mask_kind, _ptr(bm), bq, bk, mode,
+                            st, _ptr(workspace), ws_bytes, _stream(dev))
+    if rc != 0:
+        raise MiattnError(rc, "attn_fwd")
+    return o, lse
+
+
+def attn_decode(q, k_cache, v_cache, seqlens, *, scale=None, kv_chunk=0, return_lse=True,
+                out=None, lse_out=None, workspace=None):
+    """Decode attention: q [B,Hq,d] bf16 against caches [B,max_len,Hkv,d] bf16 with
+    seqlens int32 [B] (all GPU tensors). Returns (o [B,Hq,d], lse [B,Hq] or None)."""
+    _check_gpu(q, k_cache, v_cache, seqlens)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B,Hq,d]; caches [B,max_len,Hkv,d]")
+    if seqlens.dtype != torch.int32:
+        raise TypeError("seqlens must be int32")
+    B, Hq, d = q.shape
+    _, max_len, Hkv, _ = k_cache.shape
+    dev = q.device
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    q = q.contiguous()
+    seqlens = seqlens.contiguous()
+    o = torch.empty_like(q) if out is None else out
+    lse = None
+    if return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse_out is None else lse_out
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d, kv_chunk)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = (_Strides * 2)(_strides4(k_cache), _strides4(v_cache))
+    rc = library().attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o),
+                               _ptr(lse), _dtype_code(q), B, Hq, Hkv, max_len, d, scale,
+                               kv_chunk, st, _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(dev))
+    if rc != 0:
+        raise MiattnError(rc, "attn_decode")
+    return o, lse

@@ -1,0 +1,244 @@
+// C ABI of libmiattn: host-side validation, workspace sizing and dispatch.
+// Every check runs before anything is enqueued; see include/miattn.h for the
+// meaning of each argument.
+
+#include "../../include/miattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "internal.hpp"
+
+namespace {
+
+using miattn::kMaxLiveBlocks;
+using miattn::kMaxSplit;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int kstat_splits(int Nk) {
+  int n = (Nk + 255) / 256;
+  if (n < 1) n = 1;
+  if (n > kMaxSplit) n = kMaxSplit;
+  return n;
+}
+
+// Workspace of the fixed-max pre-pass, in this order:
+// part_max [B*Hkv][kMaxSplit], kbar [B*Hkv][d], part_sum [B*Hkv][kMaxSplit][d].
+size_t fwd_ws(int B, int Hkv, int d, int mode) {
+  if (mode == MIATTN_SOFTMAX_ONLINE) return 0;
+  const size_t bh = (size_t)B * Hkv;
+  size_t n = align_up(bh * kMaxSplit * sizeof(float));
+  if (mode == MIATTN_SOFTMAX_FIXED_MAX_CENTERED)
+    n += align_up(bh * d * sizeof(float)) + align_up(bh * kMaxSplit * d * sizeof(float));
+  return n;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool strides_ok(const miattn_strides& s, int64_t mult) {
+  return s.b >= 0 && s.s >= 0 && s.h >= 0 && s.b % mult == 0 && s.s % mult == 0 &&
+         s.h % mult == 0;
+}
+
+int decode_chunk(int B, int Hkv, int max_len, int kv_chunk) {
+  if (kv_chunk > 0) return kv_chunk;
+  // aim at ~16K (batch, KV head, chunk) work items, chunks of >= 256 keys
+  const int64_t items = (int64_t)(B > 0 ? B : 1) * (Hkv > 0 ? Hkv : 1);
+  int64_t n = (16384 + items - 1) / items;
+  const int64_t max_n = (max_len + 255) / 256;
+  if (n > max_n) n = max_n;
+  if (n < 1) n = 1;
+  int64_t c = (max_len + n - 1) / n;
+  c = (c + 63) / 64 * 64;
+  if (c < 64) c = 64;
+  return (int)c;
+}
+
+// Chunking of the decode cache and the bytes of its partials: part_o
+// [B][Hq][n_chunks][d] then part_lse [B][Hq][n_chunks], both fp32.
+size_t decode_layout(int B, int Hq, int Hkv, int max_len, int d, int kv_chunk, int* chunk,
+                     int* n_chunks) {
+  *chunk = decode_chunk(B, Hkv, max_len > 0 ? max_len : 1, kv_chunk);
+  *n_chunks = max_len > 0 ? (max_len + *chunk - 1) / *chunk : 1;
+  return align_up((size_t)B * Hq * *n_chunks * d * sizeof(float)) +
+         align_up((size_t)B * Hq * *n_chunks * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(int status) {
+  switch (status) {
+    case MIATTN_OK: return "ok";
+    case MIATTN_ERR_NULL: return "a required pointer is NULL";
+    case MIATTN_ERR_SHAPE: return "sizes are inconsistent or out of range";
+    case MIATTN_ERR_UNSUPPORTED: return "request not supported (dtype, head dim, alignment or limit)";
+    case MIATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case MIATTN_ERR_HIP: return "HIP runtime or launch error";
+    case MIATTN_ERR_ARG: return "invalid scalar argument (scale, mask kind or softmax mode)";
+    default: return "unknown status";
+  }
+}
+
+size_t attn_fwd_workspace_bytes(int B, int Hkv, int Nk, int d, int softmax_mode) {
+  (void)Nk;
+  if (B < 0 || Hkv < 0 || d <= 0) return 0;
+  return fwd_ws(B, Hkv, d, softmax_mode);
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
+             const uint8_t* block_mask, int block_q, int block_k, int softmax_mode,
+             const miattn_strides* strides, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  if (dtype != MIATTN_BF16 && dtype != MIATTN_F32) return MIATTN_ERR_UNSUPPORTED;
+  if (B < 0 || Nq < 0 || Nk < 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return MIATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return MIATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return MIATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return MIATTN_ERR_ARG;
+  if (mask_kind < 0 || mask_kind > (MIATTN_MASK_CAUSAL | MIATTN_MASK_BLOCK)) return MIATTN_ERR_ARG;
+  if (softmax_mode < MIATTN_SOFTMAX_ONLINE || softmax_mode > MIATTN_SOFTMAX_FIXED_MAX_CENTERED)
+    return MIATTN_ERR_ARG;
+  if (B == 0 || Nq == 0) return MIATTN_OK;  // nothing to compute
+  if (q == nullptr || o == nullptr) return MIATTN_ERR_NULL;
+  if (Nk > 0 && (k == nullptr || v == nullptr)) return MIATTN_ERR_NULL;
+
+  const bool causal = (mask_kind & MIATTN_MASK_CAUSAL) != 0;
+  const bool block = (mask_kind & MIATTN_MASK_BLOCK) != 0;
+  int nkb = 0;
+  if (block) {
+    if (block_mask == nullptr) return MIATTN_ERR_NULL;
+    if (block_q <= 0 || block_k <= 0 || block_q % 16 != 0 || block_k % 16 != 0)
+      return MIATTN_ERR_SHAPE;
+    if (Nq % block_q != 0 || Nk % block_k != 0) return MIATTN_ERR_SHAPE;
+    nkb = Nk / block_k;
+    if (nkb > kMaxLiveBlocks) return MIATTN_ERR_UNSUPPORTED;
+  }
+
+  const int64_t esz = dtype == MIATTN_BF16 ? 2 : 4;
+  const int64_t mult = 16 / esz;  // strides in whole 16-byte units
+  miattn_strides sq{(int64_t)Nq * Hq * d, (int64_t)Hq * d, d};
+  miattn_strides sk{(int64_t)Nk * Hkv * d, (int64_t)Hkv * d, d};
+  miattn_strides sv = sk, so = sq;
+  if (strides != nullptr) {
+    sq = strides[0];
+    sk = strides[1];
+    sv = strides[2];
+    so = strides[3];
+  }
+  if (!strides_ok(sq, mult) || !strides_ok(sk, mult) || !strides_ok(sv, mult) ||
+      !strides_ok(so, mult))
+    return MIATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(o) || !aligned16(k) || !aligned16(v))
+    return MIATTN_ERR_UNSUPPORTED;
+
+  const size_t need = fwd_ws(B, Hkv, d, softmax_mode);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MIATTN_ERR_WORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  miattn::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.q_sb = sq.b; p.q_ss = sq.s; p.q_sh = sq.h;
+  p.k_sb = sk.b; p.k_ss = sk.s; p.k_sh = sk.h;
+  p.v_sb = sv.b; p.v_ss = sv.s; p.v_sh = sv.h;
+  p.o_sb = so.b; p.o_ss = so.s; p.o_sh = so.h;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.causal_off = Nk - Nq;
+  p.block_mask = block_mask;
+  p.block_q = block_q; p.block_k = block_k; p.nkb = nkb;
+  // with no keys every row is empty and there is nothing to bound
+  p.fixed = Nk > 0 ? softmax_mode : MIATTN_SOFTMAX_ONLINE;
+
+  if (p.fixed != MIATTN_SOFTMAX_ONLINE) {
+    const size_t bh = (size_t)B * Hkv;
+    char* ws = (char*)workspace;
+    float* part_max = (float*)ws;
+    float* kbar = nullptr;
+    float* part_sum = nullptr;
+    if (softmax_mode == MIATTN_SOFTMAX_FIXED_MAX_CENTERED) {
+      kbar = (float*)(ws + align_up(bh * kMaxSplit * sizeof(float)));
+      part_sum = (float*)((char*)kbar + align_up(bh * d * sizeof(float)));
+    }
+    const int nsplit = kstat_splits(Nk);
+    miattn::KStatParams kp{};
+    kp.k = k; kp.k_sb = sk.b; kp.k_ss = sk.s; kp.k_sh = sk.h;
+    kp.B = B; kp.Hkv = Hkv; kp.Nk = Nk;
+    kp.nsplit = nsplit;
+    kp.keys_per_split = (Nk + nsplit - 1) / nsplit;
+    kp.part_sum = part_sum; kp.part_max = part_max; kp.kbar = kbar;
+    if (miattn::launch_kstats(kp, d, dtype == MIATTN_BF16,
+                              softmax_mode == MIATTN_SOFTMAX_FIXED_MAX_CENTERED, s) != hipSuccess)
+      return MIATTN_ERR_HIP;
+    p.ks.part_max = part_max;
+    p.ks.kbar = kbar;
+    p.ks.nsplit = nsplit;
+  }
+
+  hipError_t e = dtype == MIATTN_BF16 ? miattn::launch_fwd_bf16(p, d, causal, block, s)
+                                      : miattn::launch_fwd_f32(p, d, causal, block, s);
+  return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;
+}
+
+int attn_decode_chunk(int B, int Hkv, int max_len, int kv_chunk) {
+  return decode_chunk(B, Hkv, max_len, kv_chunk);
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d, int kv_chunk) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_len < 0 || d <= 0) return 0;
+  int chunk, n_chunks;
+  return decode_layout(B, Hq, Hkv, max_len, d, kv_chunk, &chunk, &n_chunks);
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* seqlens, void* o, float* lse, int dtype, int B, int Hq, int Hkv,
+                int max_len, int d, float scale, int kv_chunk,
+                const miattn_strides* cache_strides, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  if (dtype != MIATTN_BF16) return MIATTN_ERR_UNSUPPORTED;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || max_len < 0 || d <= 0) return MIATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return MIATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return MIATTN_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 16) return MIATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return MIATTN_ERR_ARG;
+  if (kv_chunk < 0 || (kv_chunk > 0 && kv_chunk % 64 != 0)) return MIATTN_ERR_ARG;
+  if (B == 0) return MIATTN_OK;
+  if (q == nullptr || o == nullptr || seqlens == nullptr) return MIATTN_ERR_NULL;
+  if (max_len > 0 && (k_cache == nullptr || v_cache == nullptr)) return MIATTN_ERR_NULL;
+
+  miattn_strides sk{(int64_t)max_len * Hkv * d, (int64_t)Hkv * d, d};
+  miattn_strides sv = sk;
+  if (cache_strides != nullptr) {
+    sk = cache_strides[0];
+    sv = cache_strides[1];
+  }
+  if (!strides_ok(sk, 8) || !strides_ok(sv, 8)) return MIATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return MIATTN_ERR_UNSUPPORTED;
+
+  int chunk, n_chunks;
+  const size_t need = decode_layout(B, Hq, Hkv, max_len, d, kv_chunk, &chunk, &n_chunks);
+  const size_t po = align_up((size_t)B * Hq * n_chunks * d * sizeof(float));
+  if (workspace == nullptr || workspace_bytes < need) return MIATTN_ERR_WORKSPACE;
+
+  miattn::DecodeParams p{};
+  p.q = q; p.kc = k_cache; p.vc = v_cache; p.seqlens = seqlens; p.o = o; p.lse = lse;
+  p.k_sb = sk.b; p.k_ss = sk.s; p.k_sh = sk.h;
+  p.v_sb = sv.b; p.v_ss = sv.s; p.v_sh = sv.h;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.max_len = max_len;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.chunk = chunk;
+  p.n_chunks = n_chunks;
+  p.part_o = (float*)workspace;
+  p.part_lse = (float*)((char*)workspace + po);
+  hipError_t e = miattn::launch_decode(p, d, (hipStream_t)stream);
+  return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, the MFMA
+// and LDS-transpose builtins, bf16 conversion and wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace miattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+// Fixed-max eligibility: the row max may sit at most this many nats below
+// the bound (so every row normaliser stays >= exp(-kTau) >> FLT_MIN).
+constexpr float kTau = 64.0f;
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// exp2 on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x2 cvt2(float a, float b) {
+  f32x2 x = {a, b};
+  return __builtin_convertvector(x, bf16x2);
+}
+__device__ __forceinline__ bf16x8 cvt8(float a0, float a1, float a2, float a3, float a4,
+                                       float a5, float a6, float a7) {
+  bf16x2 p0 = cvt2(a0, a1), p1 = cvt2(a2, a3), p2 = cvt2(a4, a5), p3 = cvt2(a6, a7);
+  bf16x8 r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  return r;
+}
+__device__ __forceinline__ bf16x4 cvt4(float a0, float a1, float a2, float a3) {
+  bf16x2 p0 = cvt2(a0, a1), p1 = cvt2(a2, a3);
+  bf16x4 r = {p0[0], p0[1], p1[0], p1[1]};
+  return r;
+}
+
+__device__ __forceinline__ float bf2f(__bf16 x) { return (float)x; }
+
+// D = A * B + C, 32x32 output, K = 16, bf16 inputs (8 per lane), fp32 accum.
+// A[i][k] sits in lane i + 32*(k/8), element k%8; B[k][j] in lane j + 32*(k/8);
+// C[i][j] in lane j + 32*((i/4)%2), register (i%4) + 4*(i/8).
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// 16x16 output, K = 32: A[i][k] in lane i + 16*(k/8), element k%8;
+// C[i][j] in lane j + 16*(i/4), register i%4.
+__device__ __forceinline__ f32x4 mfma16k32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 16x16 output, K = 16: A[i][k] in lane i + 16*(k/4), element k%4.
+__device__ __forceinline__ f32x4 mfma16k16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane i receives, as element j (j = 0..3), element i%4 of the 8 bytes that
+// lane 4*j + i/4 of the same group addressed.
+__device__ __forceinline__ s16x4 lds_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
+  return v;
+}
+
+}  // namespace miattn

@@ -1,0 +1,456 @@
+// Prefill attention, bf16 inputs, fp32 accumulation, on gfx950 MFMA.
+//
+// The method: exact attention evaluated block by block with a running row
+// max m and running sum l, so S = Q K^T and P never leave the chip
+// ("플래시어텐션: 메모리를 아끼는 정확한 어텐션", §2 타일링 and §3 알고리즘;
+// "Attention Mechanism Optimization for Efficient LLM Inference",
+// "FlashAttention / Tiling" and "Online-Softmax").
+//
+// Layout of the work (our design for CDNA4, not the pages' CUDA loop order):
+//  * One workgroup = 4 waves = 128 query rows of one (batch, query head); the
+//    Q tile stays in VGPRs, O accumulates in VGPRs; K/V tiles of 64 keys are
+//    streamed HBM -> VGPR -> LDS, double-buffered (the next tile's global
+//    loads are in flight while the current tile is consumed).
+//  * Each wave owns 32 query rows and computes S^T = K Q^T with
+//    v_mfma_f32_32x32x16_bf16, so every lane holds the scores of ONE query
+//    for 16 keys of a 32-key block: the row max needs one cross-lane step
+//    (lane ^ 32) and the row sum needs none until the end.
+//  * P^T feeds O^T = V^T P^T straight from the accumulator registers (the key
+//    order inside each 16-key step is permuted so the accumulator layout is
+//    the MFMA B-operand layout); V^T comes from the row-major LDS tile through
+//    ds_read_b64_tr_b16, so V is never transposed in memory.
+//  * Causal: tiles wholly above a wave's rows are skipped, the element rule is
+//    applied only on tiles that cross the diagonal. Block mask: the workgroup
+//    walks only the union of its rows' live key blocks; a wave whose rows all
+//    share that live set applies no mask at all (blocks are never partial).
+//  * Fixed-max softmax (TPU attention guide, 4단계): the per-row bound
+//    M_i = scale*|q_i|*rho replaces the running max, removing the max
+//    reduction and the accumulator rescale; a 32-row group whose bound is too
+//    loose falls back to the running max.
+//  * Workgroup order: heaviest causal tiles first; the query heads sharing a
+//    KV head land on the same XCD (blockIdx % 8) so K/V are reused in its L2.
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace miattn {
+
+namespace {
+
+constexpr int BQ = 128;  // query rows per workgroup
+constexpr int BK = 64;   // keys per tile
+constexpr int NT = 256;  // threads per workgroup
+
+// LDS swizzles on 16-byte chunks, chosen so the MFMA-side reads hit distinct
+// banks: K is read 16 rows x one chunk per 16 lanes; V is read by the
+// transpose load 4 rows x 2 chunks per 16 lanes.
+template <int D>
+__device__ __forceinline__ int kswz(int r, int ch) {
+  if constexpr (D == 128) return ch ^ (r & 15);
+  else return ch ^ ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int r, int ch) {
+  if constexpr (D == 128) return ch ^ ((r & 3) << 2);
+  else return ch ^ (((r >> 1) & 1) << 2);
+}
+
+// Hardware workgroup id -> (logical tile X, member g of the head group).
+// Groups of 8*G consecutive ids keep the G query heads of one KV head on one
+// XCD (ids are dealt round-robin over the 8 XCDs).
+__device__ __forceinline__ void map_workgroup(int i, int G, int nX, int& X, int& g) {
+  const int chunk = 8 * G;
+  const int full = nX >> 3;
+  const int c = i / chunk;
+  if (c < full) {
+    const int r = i - c * chunk;
+    X = c * 8 + (r & 7);
+    g = r >> 3;
+  } else {
+    const int rr = i - full * chunk;
+    X = full * 8 + rr / G;
+    g = rr - (rr / G) * G;
+  }
+}
+
+template <int D, bool CAUSAL, bool BLOCK>
+__global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
+  constexpr int CH = D / 8;          // 16-byte chunks per K/V row
+  constexpr int KSTEPS = D / 16;     // k-steps of the S^T MFMA
+  constexpr int MB = D / 32;         // 32-row blocks of O^T
+  constexpr int RPP = NT / CH;       // tile rows staged per pass
+  constexpr int NPASS = BK / RPP;    // staging passes per tile
+
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2 * BK * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[2 * BK * D];
+  __shared__ short sLive[BLOCK ? kMaxLiveBlocks : 1];
+  __shared__ int sCount;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c = lane & 31;  // query column of this lane
+  const int h = lane >> 5;  // which half of each 8-row group of keys
+
+  const int G = p.Hq / p.Hkv;
+  int X, g;
+  map_workgroup(blockIdx.x, G, p.n_qtiles * p.B * p.Hkv, X, g);
+  const int hkv = X % p.Hkv;
+  const int t2 = X / p.Hkv;
+  const int b = t2 % p.B;
+  const int qt_rank = t2 / p.B;
+  const int qt = CAUSAL ? (p.n_qtiles - 1 - qt_rank) : qt_rank;
+  const int hq = hkv * G + g;
+
+  const int q_start = qt * BQ;
+  const int q_end = min(q_start + BQ, p.Nq);
+  const int q0 = q_start + wave * 32;
+  const int qrow = q0 + c;
+  const bool row_ok = qrow < p.Nq;
+  const int wave_last = min(q0 + 31, p.Nq - 1);  // last valid row of the wave
+
+  const __bf16* __restrict__ qg = (const __bf16*)p.q;
+  const __bf16* __restrict__ kg = (const __bf16*)p.k + b * p.k_sb + hkv * p.k_sh;
+  const __bf16* __restrict__ vg = (const __bf16*)p.v + b * p.v_sb + hkv * p.v_sh;
+
+  // ---- Q fragments: lane (c, h), k-step t holds q[qrow][16t + 8h .. +8]
+  bf16x8 qf[KSTEPS];
+  {
+    const __bf16* qp = qg + b * p.q_sb + (int64_t)qrow * p.q_ss + hq * p.q_sh + 8 * h;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      bf16x8 z = {};
+      qf[t] = row_ok ? *(const bf16x8*)(qp + 16 * t) : z;
+    }
+  }
+
+  // ---- key range of this workgroup
+  int kv_end = p.Nk;   // dense: keys [0, kv_end)
+  int n_live_keys = 0; // block: number of keys in the live-block list
+  if constexpr (!BLOCK) {
+    if constexpr (CAUSAL) kv_end = min(p.Nk, max(0, q_end - 1 + p.causal_off + 1));
+  } else {
+    // union of the live key blocks of the block rows this workgroup covers,
+    // compacted in key order into sLive (wave 0, 64 blocks per step)
+    if (wave == 0) {
+      const int qb0 = q_start / p.block_q;
+      const int qb1 = (q_end - 1) / p.block_q;
+      int count = 0;
+      for (int base = 0; base < p.nkb; base += 64) {
+        const int kb = base + lane;
+        bool live = false;
+        if (kb < p.nkb)
+          for (int qb = qb0; qb <= qb1; ++qb) live |= p.block_mask[(int64_t)qb * p.nkb + kb] != 0;
+        const uint64_t bal = __ballot(live);
+        const int pos = __popcll(bal & ((1ull << lane) - 1ull));
+        if (live) sLive[count + pos] = (short)kb;
+        count += __popcll(bal);
+      }
+      if (lane == 0) sCount = count;
+    }
+    __syncthreads();
+    n_live_keys = sCount * p.block_k;
+  }
+  const int n_keys = BLOCK ? n_live_keys : kv_end;
+  const int n_tiles = (n_keys + BK - 1) / BK;
+
+  // BLOCK: does every row of this wave see every block of the union?
+  bool wave_uniform = true;
+  int my_qb = 0;
+  if constexpr (BLOCK) {
+    my_qb = (row_ok ? qrow : wave_last) / p.block_q;
+    bool ok = true;
+    if (q0 < p.Nq) {
+      const int wqb0 = q0 / p.block_q, wqb1 = wave_last / p.block_q;
+      for (int i = lane; i < sCount; i += 64)
+        for (int qb = wqb0; qb <= wqb1; ++qb)
+          ok &= p.block_mask[(int64_t)qb * p.nkb + sLive[i]] != 0;
+    }
+    wave_uniform = __ballot(!ok) == 0ull;
+  }
+
+  // ---- fixed-max bound for this lane's row, and the group's eligibility
+  bool fixed = false;
+  float m_fix = 0.f;  // bound in log2 units
+  if (p.fixed) {
+    float qq = 0.f;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = bf2f(qf[t][e]);
+        qq += x * x;
+      }
+    qq += shfl_xor(qq, 32);
+    const float qn = sqrtf(qq);
+    // rho^2 = max over the key splits of the partial maxima
+    const int64_t bh = (int64_t)b * p.Hkv + hkv;
+    float r2 = lane < p.ks.nsplit ? p.ks.part_max[bh * kMaxSplit + lane] : 0.f;
+    r2 = wave_max(r2);
+    const float rho = sqrtf(r2);
+    float qk = 0.f;
+    if (p.fixed == 2) {
+      const float* kb = p.ks.kbar + bh * D + 8 * h;
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qk += bf2f(qf[t][e]) * kb[16 * t + e];
+      qk += shfl_xor(qk, 32);
+    }
+    m_fix = p.scale * (qk + qn * rho) * kLog2e;
+    const float gap = row_ok ? 2.f * p.scale * qn * rho : 0.f;
+    fixed = wave_max(gap) <= kTau;
+  }
+
+  // ---- staging of one K/V tile: thread -> (row r, chunk ch)
+  u32x4 kreg[NPASS], vreg[NPASS];
+  const int st_row = tid / CH;
+  const int st_ch = tid - st_row * CH;
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < NPASS; ++i) {
+      const int r = st_row + RPP * i;
+      int key;
+      bool ok;
+      if constexpr (!BLOCK) {
+        key = t * BK + r;
+        ok = key < kv_end;
+      } else {
+        const int L = t * BK + r;
+        ok = L < n_live_keys;
+        const int blk = ok ? L / p.block_k : 0;
+        key = ok ? (int)sLive[blk] * p.block_k + (L - blk * p.block_k) : 0;
+      }
+      u32x4 z = {0u, 0u, 0u, 0u};
+      kreg[i] = ok ? *(const u32x4*)(kg + (int64_t)key * p.k_ss + st_ch * 8) : z;
+      vreg[i] = ok ? *(const u32x4*)(vg + (int64_t)key * p.v_ss + st_ch * 8) : z;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NPASS; ++i) {
+      const int r = st_row + RPP * i;
+      *(u32x4*)(sK + buf * BK * D + r * D + kswz<D>(r, st_ch) * 8) = kreg[i];
+      *(u32x4*)(sV + buf * BK * D + r * D + vswz<D>(r, st_ch) * 8) = vreg[i];
+    }
+  };
+
+  // ---- accumulators
+  f32x16 oacc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[mb][r] = 0.f;
+  float m_run = kNegInf;  // running max (log2 units), online mode
+  float l_run = 0.f;      // this lane's partial row sum (half of the keys)
+
+  // per-lane address pieces for the V^T transpose reads (see PV below)
+  const int tr_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_ch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_half = 4 * (lane & 1);
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) load_tile(t + 1);
+
+    // ---- what this wave has to do with this tile
+    // state 0: nothing visible, 1: everything visible, 2: apply the mask
+    int state = 1;
+    bool grp_live[4] = {true, true, true, true};  // BLOCK, per 16-key group
+    const int tile_k0 = t * BK;
+    if (q0 >= p.Nq) {
+      state = 0;
+    } else if constexpr (!BLOCK) {
+      if (CAUSAL) {
+        if (tile_k0 > wave_last + p.causal_off) state = 0;
+        else if (tile_k0 + BK - 1 > q0 + p.causal_off) state = 2;
+      }
+      if (state == 1 && tile_k0 + BK > p.Nk) state = 2;
+    } else {
+      if (!wave_uniform) {
+        bool any = false;
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          const int L = tile_k0 + 16 * gi;
+          bool live = false;
+          if (L < n_live_keys && row_ok)
+            live = p.block_mask[(int64_t)my_qb * p.nkb + sLive[L / p.block_k]] != 0;
+          grp_live[gi] = live;
+          any |= live;
+        }
+        state = __ballot(any) ? 2 : 0;
+      } else if (CAUSAL || tile_k0 + BK > n_live_keys) {
+        state = 2;
+      }
+    }
+
+    if (state != 0) {
+      // ---- S^T = K Q^T for two 32-key blocks
+      f32x16 s[2];
+      const __bf16* sk = sK + buf * BK * D;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        const int row = 32 * kb + c;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          const bf16x8 kf = *(const bf16x8*)(sk + row * D + kswz<D>(row, 2 * ks + h) * 8);
+          s[kb] = mfma32(kf, qf[ks], s[kb]);
+        }
+      }
+
+      // ---- scale to log2 units and mask. Lane (c, h), register r of block
+      // kb holds key 32kb + 8(r/4) + 4h + r%4 of the tile, query qrow.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] *= p.scale_log2;
+      if (state == 2) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);  // key within tile
+            bool ok;
+            if constexpr (!BLOCK) {
+              const int key = tile_k0 + kk;
+              ok = key < p.Nk;
+              if (CAUSAL) ok = ok && key <= qrow + p.causal_off;
+            } else {
+              const int L = tile_k0 + kk;
+              ok = L < n_live_keys && grp_live[kk >> 4];
+              if (CAUSAL && ok) {
+                const int blk = L / p.block_k;
+                const int key = (int)sLive[blk] * p.block_k + (L - blk * p.block_k);
+                ok = key <= qrow + p.causal_off;
+              }
+            }
+            if (!ok) s[kb][r] = kNegInf;
+          }
+      }
+
+      // ---- softmax update
+      if (!fixed) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == kNegInf ? 0.f : m_new;
+        const float alpha = ex2(m_run - m_use);
+        m_run = m_new;
+        if (__ballot(alpha != 1.f)) {
+          l_run *= alpha;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = ex2(s[kb][r] - m_use);
+            s[kb][r] = e;
+            l_run += e;
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = ex2(s[kb][r] - m_fix);
+            s[kb][r] = e;
+            l_run += e;
+          }
+      }
+
+      // ---- O^T += V^T P^T, four 16-key steps. Step u uses registers
+      // 8(u%2) .. +7 of block u/2: keys 16u + 4h + e (e < 4) and
+      // 16u + 8 + 4h + (e - 4) (e >= 4) for query c -- the B operand as is.
+      const __bf16* sv = sV + buf * BK * D;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const f32x16& sb = s[u >> 1];
+        const int o8 = 8 * (u & 1);
+        const bf16x8 pf = cvt8(sb[o8 + 0], sb[o8 + 1], sb[o8 + 2], sb[o8 + 3], sb[o8 + 4],
+                               sb[o8 + 5], sb[o8 + 6], sb[o8 + 7]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          // A operand (V^T rows 32mb..+31, the same 16 keys): two transpose
+          // reads, keys 16u + 8rr + 4h' + j for the lanes' groups.
+          s16x4 lo, hi;
+          {
+            const int row = 16 * u + tr_row;
+            const int ch = 4 * mb + tr_ch;
+            lo = lds_tr16(sv + row * D + vswz<D>(row, ch) * 8 + tr_half);
+          }
+          {
+            const int row = 16 * u + 8 + tr_row;
+            const int ch = 4 * mb + tr_ch;
+            hi = lds_tr16(sv + row * D + vswz<D>(row, ch) * 8 + tr_half);
+          }
+          const s16x8 a16 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[mb] = mfma32(__builtin_bit_cast(bf16x8, a16), pf, oacc[mb]);
+        }
+      }
+    }
+
+    if (t + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2
+  const float l_tot = l_run + shfl_xor(l_run, 32);
+  const bool live = l_tot > 0.f;
+  const float inv = live ? 1.f / l_tot : 0.f;
+  if (row_ok) {
+    __bf16* op = (__bf16*)p.o + b * p.o_sb + (int64_t)qrow * p.o_ss + hq * p.o_sh;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const bf16x4 v4 = cvt4(oacc[mb][4 * jj + 0] * inv, oacc[mb][4 * jj + 1] * inv,
+                               oacc[mb][4 * jj + 2] * inv, oacc[mb][4 * jj + 3] * inv);
+        *(bf16x4*)(op + 32 * mb + 8 * jj + 4 * h) = v4;
+      }
+    if (p.lse != nullptr && h == 0) {
+      const float m_ref = fixed ? m_fix : m_run;
+      p.lse[((int64_t)b * p.Hq + hq) * p.Nq + qrow] = live ? (m_ref + log2f(l_tot)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+template <int D, bool CAUSAL, bool BLOCK>
+hipError_t launch_one(const FwdParams& p, hipStream_t s) {
+  const int grid = p.n_qtiles * p.B * p.Hq;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BLOCK>), dim3(grid), dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdParams& p0, int d, bool causal, bool block, hipStream_t s) {
+  FwdParams p = p0;
+  p.n_qtiles = (p.Nq + BQ - 1) / BQ;
+  if (p.n_qtiles == 0 || p.B == 0) return hipSuccess;
+#define MIATTN_DISPATCH(DD)                                                     \
+  if (causal && block) return launch_one<DD, true, true>(p, s);                \
+  if (causal) return launch_one<DD, true, false>(p, s);                        \
+  if (block) return launch_one<DD, false, true>(p, s);                         \
+  return launch_one<DD, false, false>(p, s);
+  if (d == 64) { MIATTN_DISPATCH(64) }
+  MIATTN_DISPATCH(128)
+#undef MIATTN_DISPATCH
+}
+
+}  // namespace miattn

@@ -1,0 +1,156 @@
+/* miattn -- exact IO-aware attention for MI355X (gfx950), C ABI.
+ *
+ * What is computed: exact scaled dot-product attention
+ *     O = softmax(scale * Q K^T) V
+ * ("Attention Mechanism Optimization for Efficient LLM Inference",
+ * "Background: Scaled Dot-Product Attention"), evaluated tile by tile with the
+ * running-max / running-sum softmax so the score and probability matrices are
+ * never stored ("플래시어텐션: 메모리를 아끼는 정확한 어텐션", §2 타일링 and §3
+ * 알고리즘, Theorem 1). Alongside O the library returns the per-row
+ * log-sum-exp LSE = m + ln(l) of the scaled scores (natural log), the only
+ * statistic the method keeps besides O (same page, §4 재계산).
+ *
+ * Conventions common to every entry point
+ *  - Pointers marked "device" are HIP device pointers; the caller owns them.
+ *    The library allocates nothing, frees nothing and keeps no mutable global
+ *    state, so calls on different streams may run concurrently.
+ *  - Layout is [batch, seq, heads, d] ("Multi-Query Attention (MQA)",
+ *    "Comparison"), d contiguous (stride 1). Other strides are given in
+ *    elements through miattn_strides; NULL means packed.
+ *  - Head groups: query head h reads KV head h / (Hq / Hkv)
+ *    ("Grouped-Query Attention (GQA)": contiguous groups; Hkv = 1 is MQA,
+ *    Hkv = Hq is MHA). Hq must be a multiple of Hkv.
+ *  - Arguments are validated on the host before anything is launched; a
+ *    nonzero status means nothing was enqueued. Kernels are enqueued on
+ *    `stream` (a hipStream_t; NULL = the null stream) and the call returns
+ *    without synchronising. MIATTN_ERR_HIP reports a launch error; faults
+ *    inside kernels surface at the caller's next synchronisation.
+ *  - No atomics: the same inputs and arguments give bitwise identical outputs.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef MIATTN_H
+#define MIATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  MIATTN_OK = 0,
+  MIATTN_ERR_NULL = 1,        /* a required pointer is NULL                  */
+  MIATTN_ERR_SHAPE = 2,       /* sizes inconsistent or out of range          */
+  MIATTN_ERR_UNSUPPORTED = 3, /* valid request this build does not implement */
+  MIATTN_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required  */
+  MIATTN_ERR_HIP = 5,         /* a HIP runtime call or launch failed         */
+  MIATTN_ERR_ARG = 6          /* a scalar argument is invalid (scale, mode)  */
+};
+
+/* Element types. */
+enum { MIATTN_BF16 = 0, MIATTN_F32 = 1 };
+
+/* Mask kinds (bit flags; CAUSAL | BLOCK combines both rules). */
+enum { MIATTN_MASK_NONE = 0, MIATTN_MASK_CAUSAL = 1, MIATTN_MASK_BLOCK = 2 };
+
+/* Softmax evaluation. ONLINE keeps a running row max and rescales ("Online-
+ * Softmax"). FIXED_MAX subtracts a per-row upper bound on the logits fixed
+ * before the key loop, scale * |q_i| * max_j |k_j| (Cauchy-Schwarz);
+ * FIXED_MAX_CENTERED uses scale * (q_i . kbar + |q_i| * max_j |k_j - kbar|)
+ * with kbar the mean key ("TPU attention 최적화 실전 가이드", 4단계). Both are
+ * checked per group of 32 query rows of one head: every logit of row i lies
+ * within 2 * scale * |q_i| * rho below the bound (rho = max|k_j| or
+ * max|k_j - kbar|), and a group where that gap could exceed 64 nats falls back
+ * to ONLINE, so exp never underflows the row. The result is the same exact
+ * attention either way. */
+enum {
+  MIATTN_SOFTMAX_ONLINE = 0,
+  MIATTN_SOFTMAX_FIXED_MAX = 1,
+  MIATTN_SOFTMAX_FIXED_MAX_CENTERED = 2
+};
+
+/* Element strides of a [B, S, H, d] view (d has stride 1). */
+typedef struct {
+  int64_t b, s, h;
+} miattn_strides;
+
+/* Bytes of device workspace attn_fwd needs (0 for ONLINE). */
+size_t attn_fwd_workspace_bytes(int B, int Hkv, int Nk, int d, int softmax_mode);
+
+/* Prefill / full-sequence attention.
+ *
+ * q      device, [B, Nq, Hq, d], dtype          (read)
+ * k, v   device, [B, Nk, Hkv, d], dtype         (read)
+ * o      device, [B, Nq, Hq, d], dtype          (written)
+ * lse    device, float [B, Hq, Nq] or NULL      (written: m + ln l, natural log)
+ * dtype  MIATTN_BF16 (bf16 MFMA, fp32 accumulation; P rounded to bf16 for the
+ *        P V product) or MIATTN_F32 (fp32 throughout)
+ * d      64 or 128
+ * scale  > 0 and finite; usually 1/sqrt(d)
+ * mask_kind  MIATTN_MASK_* flags.
+ *        CAUSAL: key j is visible to query i iff j <= i + (Nk - Nq) (rows
+ *        aligned at the end, so a single query sees every key).
+ *        BLOCK: block_mask (device, uint8 [Nq/block_q, Nk/block_k], row-major,
+ *        shared by every batch and head); pairs in a zero block are excluded,
+ *        pairs in a nonzero block are included ("플래시어텐션..." §6 블록 희소).
+ *        block_q and block_k must be multiples of 16 dividing Nq and Nk, so
+ *        no block is partial ("TPU attention 최적화 실전 가이드", 3단계), and
+ *        Nk / block_k <= 4096.
+ * softmax_mode  MIATTN_SOFTMAX_*
+ * strides  NULL (packed) or an array of 4: q, k, v, o
+ * workspace, workspace_bytes  device scratch of at least
+ *        attn_fwd_workspace_bytes(B, Hkv, Nk, d, softmax_mode) bytes
+ *        (may be NULL / 0 for ONLINE)
+ * stream   hipStream_t
+ * A query row with no visible key yields O = 0 and LSE = -inf. Positions a
+ * mask excludes never influence the result, whatever their values. */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+             int mask_kind, const uint8_t* block_mask, int block_q, int block_k,
+             int softmax_mode, const miattn_strides* strides,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace attn_decode needs for the split-K partials
+ * (0 when the sizes are invalid). */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d, int kv_chunk);
+
+/* Decode: one new query token per sequence against a contiguous KV cache
+ * ("Role of KV Cache"; "Two Phases of Inference", Decode): query token b
+ * attends to the first seqlens[b] cached keys of its sequence.
+ *
+ * The cache is split into chunks of kv_chunk keys; each chunk's normalised
+ * output and LSE are written to the workspace and merged with the block rule
+ * of "플래시어텐션..." §2 타일링 (weights exp(LSE_c - LSE)).
+ *
+ * q        device, [B, Hq, d] bf16, packed       (read)
+ * k_cache, v_cache  device, [B, max_len, Hkv, d] bf16 (read; rows at or past
+ *          seqlens[b] are never read)
+ * seqlens  device, int32 [B], each in [0, max_len] (precondition, not checked
+ *          on the host: the values live on the device)
+ * o        device, [B, Hq, d] bf16, packed        (written)
+ * lse      device, float [B, Hq] or NULL          (written)
+ * dtype    MIATTN_BF16
+ * d        64 or 128; Hq / Hkv <= 16
+ * kv_chunk keys per split, a positive multiple of 64, or 0 for automatic
+ * cache_strides  NULL (packed) or an array of 2: k_cache, v_cache
+ * workspace  device, at least attn_decode_workspace_bytes(...) bytes
+ * A sequence of length 0 yields O = 0 and LSE = -inf. */
+int attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* seqlens, void* o, float* lse, int dtype, int B,
+                int Hq, int Hkv, int max_len, int d, float scale, int kv_chunk,
+                const miattn_strides* cache_strides, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* The key chunk attn_decode uses for kv_chunk = 0 (or the value given). */
+int attn_decode_chunk(int B, int Hkv, int max_len, int kv_chunk);
+
+/* Static description of a status code. */
+const char* attn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIATTN_H */

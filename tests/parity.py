@@ -1,0 +1,56 @@
+"""Comparison helpers for the GPU parity tests (HIP path vs the fp64 oracle).
+
+Tolerances: bf16 inputs with fp32 accumulation -- O max-abs <= 1e-2 and
+relative Frobenius <= 5e-3 over the tensor, LSE max-abs <= 1e-3; fp32 inputs --
+O and LSE max-abs <= 1e-5. Rows with no visible key must be exactly O = 0 and
+LSE = -inf on both sides.
+"""
+
+import numpy as np
+import torch
+
+TOL = {
+    "bf16": dict(o_abs=1e-2, o_rel_fro=5e-3, lse_abs=1e-3),
+    "f32": dict(o_abs=1e-5, o_rel_fro=None, lse_abs=1e-5),
+}
+
+
+def to64(t):
+    if isinstance(t, torch.Tensor):
+        return t.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+def check(o_gpu, O_ref, lse_gpu=None, LSE_ref=None, dtype="bf16", where=""):
+    tol = TOL[dtype]
+    o = to64(o_gpu)
+    assert o.shape == O_ref.shape, (o.shape, O_ref.shape)
+    assert np.isfinite(o).all(), f"{where}: non-finite output"
+    err = np.abs(o - O_ref)
+    mx = float(err.max()) if err.size else 0.0
+    assert mx <= tol["o_abs"], f"{where}: O max-abs {mx:.3e} > {tol['o_abs']}"
+    if tol["o_rel_fro"] is not None and err.size:
+        rel = float(np.linalg.norm(o - O_ref) / max(np.linalg.norm(O_ref), 1e-300))
+        assert rel <= tol["o_rel_fro"], f"{where}: O rel-Frobenius {rel:.3e} > {tol['o_rel_fro']}"
+    if lse_gpu is not None:
+        l = to64(lse_gpu)
+        assert l.shape == LSE_ref.shape, (l.shape, LSE_ref.shape)
+        fin = np.isfinite(LSE_ref)
+        assert np.array_equal(np.isneginf(l), np.isneginf(LSE_ref)), f"{where}: -inf rows differ"
+        if fin.any():
+            le = float(np.abs(l[fin] - LSE_ref[fin]).max())
+            assert le <= tol["lse_abs"], f"{where}: LSE max-abs {le:.3e} > {tol['lse_abs']}"
+    return mx
+
+
+def sample_rows(n, tile=128, extra=16, seed=0, boundaries=()):
+    """First and last rows, rows around every tile edge up to a cap, the given
+    boundaries (and their neighbours), plus random rows -- sorted, unique."""
+    rng = np.random.default_rng(seed)
+    rows = {0, n - 1}
+    for e in list(range(tile, n, tile))[:8] + list(range(tile, n, tile))[-4:]:
+        rows |= {e - 1, e}
+    for e in boundaries:
+        rows |= {max(0, e - 1), min(n - 1, e)}
+    rows |= set(rng.integers(0, n, size=extra).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < n))

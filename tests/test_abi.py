@@ -1,0 +1,106 @@
+"""The C-ABI library: it loads, exports every function include/miattn.h declares,
+and its host-side validation answers without touching the GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+from exact_io_aware_attn_amd import binding as bd
+
+HEADER = os.path.join(ROOT, "include", "miattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(bd.LIB_PATH),
+                                reason="libmiattn.so not built (python -m exact_io_aware_attn_amd.build)")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\**\s*([A-Za-z_]\w*)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == sorted(bd._EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(bd.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(7):
+        assert bd.attn_status_str(code)
+    assert bd.attn_status_str(0) == "ok"
+    assert bd.attn_status_str(99) == "unknown status"
+
+
+def test_workspace_sizes():
+    assert bd.attn_fwd_workspace_bytes(1, 24, 14080, 128, 0) == 0
+    plain = bd.attn_fwd_workspace_bytes(1, 24, 14080, 128, 1)
+    centred = bd.attn_fwd_workspace_bytes(1, 24, 14080, 128, 2)
+    assert plain >= 24 * 64 * 4 and centred > plain
+    ws = bd.attn_decode_workspace_bytes(64, 32, 8, 32768, 128, 0)
+    chunk = bd.attn_decode_chunk(64, 8, 32768, 0)
+    n = -(-32768 // chunk)
+    assert chunk % 64 == 0 and ws >= 64 * 32 * n * 129 * 4
+    assert bd.attn_decode_chunk(64, 8, 32768, 512) == 512
+
+
+def _fwd(**kw):
+    a = dict(q=16, k=16, v=16, o=16, lse=None, dtype=0, B=1, Hq=4, Hkv=2, Nq=64, Nk=64, d=64,
+             scale=0.125, mask_kind=0, block_mask=None, block_q=0, block_k=0, mode=0,
+             strides=None, ws=None, ws_bytes=0)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return bd.library().attn_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["o"]), P(a["lse"]), a["dtype"],
+                                 a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                                 a["mask_kind"], P(a["block_mask"]), a["block_q"], a["block_k"],
+                                 a["mode"], a["strides"], P(a["ws"]), a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), 3), (dict(d=96), 3), (dict(Hq=3), 2), (dict(B=-1), 2),
+    (dict(scale=0.0), 6), (dict(scale=float("nan")), 6), (dict(mask_kind=4), 6),
+    (dict(mode=3), 6), (dict(q=None), 1),
+    (dict(mask_kind=2, block_mask=16, block_q=8, block_k=16), 2),
+    (dict(mask_kind=2, block_mask=16, block_q=48, block_k=16), 2),
+    (dict(mask_kind=2, block_mask=None, block_q=16, block_k=16), 1),
+    (dict(mode=1), 4), (dict(q=18), 3),
+    (dict(B=0), 0), (dict(Nq=0), 0),
+])
+def test_fwd_validation(kw, status):
+    """Each of these returns before anything is enqueued (no GPU needed)."""
+    assert _fwd(**kw) == status
+
+
+def test_fwd_rejects_unaligned_strides():
+    st = (bd._Strides * 4)(bd._Strides(4096, 256, 63), bd._Strides(4096, 128, 64),
+                           bd._Strides(4096, 128, 64), bd._Strides(4096, 256, 64))
+    assert _fwd(strides=st) == 3
+
+
+def _dec(**kw):
+    a = dict(q=16, k=16, v=16, seqlens=16, o=16, lse=None, dtype=0, B=2, Hq=8, Hkv=2,
+             max_len=256, d=128, scale=0.1, chunk=0, ws=None, ws_bytes=0)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return bd.library().attn_decode(P(a["q"]), P(a["k"]), P(a["v"]), P(a["seqlens"]), P(a["o"]),
+                                    P(a["lse"]), a["dtype"], a["B"], a["Hq"], a["Hkv"],
+                                    a["max_len"], a["d"], a["scale"], a["chunk"], None,
+                                    P(a["ws"]), a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=1), 3), (dict(d=80), 3), (dict(Hq=7), 2), (dict(Hq=34, Hkv=2), 3),
+    (dict(scale=-1.0), 6), (dict(chunk=100), 6), (dict(seqlens=None), 1),
+    (dict(ws=None), 4), (dict(B=0), 0),
+])
+def test_decode_validation(kw, status):
+    assert _dec(**kw) == status

@@ -1,0 +1,95 @@
+"""attn_decode on the GPU against the fp64 oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_attn_amd import attn_decode
+from exact_io_aware_attn_amd.inputs import WORKLOADS, decode_inputs
+
+from parity import check, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run(seqlens, q, kc, vc, **kw):
+    o, lse = attn_decode(q.to(DEV), kc.to(DEV), vc.to(DEV), seqlens.to(DEV), **kw)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4), (16, 1)])
+@pytest.mark.parametrize("kv_chunk", [0, 64, 192])
+def test_decode_small(d, Hq, Hkv, kv_chunk):
+    seqlens, q, kc, vc = decode_inputs(5, Hq, Hkv, 700, d, torch.bfloat16, seed=d + Hq, len_lo=1, len_hi=700)
+    seqlens[0] = 700
+    seqlens[1] = 1
+    seqlens[2] = 64
+    o, lse = _run(seqlens, q, kc, vc, kv_chunk=kv_chunk)
+    O, L = oracle.decode(to64(q), to64(kc), to64(vc), seqlens.numpy(), 1 / math.sqrt(d))
+    check(o, O, lse, L, where=f"decode d={d} H={Hq}/{Hkv} chunk={kv_chunk}")
+
+
+def test_decode_zero_length():
+    seqlens, q, kc, vc = decode_inputs(3, 8, 2, 256, 128, torch.bfloat16, seed=1, len_lo=0, len_hi=256)
+    seqlens[1] = 0
+    o, lse = _run(seqlens, q, kc, vc)
+    O, L = oracle.decode(to64(q), to64(kc), to64(vc), seqlens.numpy(), 1 / math.sqrt(128))
+    check(o, O, lse, L, where="zero length")
+    assert (o[1].float() == 0).all() and torch.isneginf(lse[1]).all()
+
+
+def test_decode_rows_past_length_never_read():
+    """NaN in every cache row at or past seqlens[b]: output bit-identical to the
+    run with zeros there."""
+    seqlens, q, kc, vc = decode_inputs(4, 8, 2, 512, 128, torch.bfloat16, seed=2, len_lo=1, len_hi=500)
+    kz, vz, kn, vn = kc.clone(), vc.clone(), kc.clone(), vc.clone()
+    for b, n in enumerate(seqlens.tolist()):
+        kz[b, n:] = 0
+        vz[b, n:] = 0
+        kn[b, n:] = float("nan")
+        vn[b, n:] = float("nan")
+    o1, l1 = _run(seqlens, q, kz, vz)
+    o2, l2 = _run(seqlens, q, kn, vn)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.isfinite(o2.float()).all()
+
+
+def test_decode_repeatable_bitwise():
+    seqlens, q, kc, vc = decode_inputs(4, 8, 2, 1000, 128, torch.bfloat16, seed=3, len_lo=100, len_hi=1000)
+    o1, l1 = _run(seqlens, q, kc, vc)
+    o2, l2 = _run(seqlens, q, kc, vc)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_equals_prefill_with_one_query():
+    """Decode against cache[:len] equals attn_fwd with Nq = 1 on that prefix."""
+    from exact_io_aware_attn_amd import attn_fwd
+    seqlens, q, kc, vc = decode_inputs(2, 8, 2, 300, 128, torch.bfloat16, seed=4, len_lo=200, len_hi=300)
+    o, _ = _run(seqlens, q, kc, vc)
+    for b, n in enumerate(seqlens.tolist()):
+        of, _ = attn_fwd(q[b:b + 1, None].to(DEV), kc[b:b + 1, :n].to(DEV), vc[b:b + 1, :n].to(DEV), causal=True)
+        torch.cuda.synchronize()
+        assert (o[b].float() - of[0, 0].float()).abs().max() <= 1e-2
+
+
+def test_full_gqa_decode_b64():
+    """The full decode workload on the GPU, checked on sampled sequences: the
+    shortest, the longest and a few more, all 32 query heads each."""
+    w = WORKLOADS["gqa-decode-b64"]
+    seqlens, q, kc, vc = decode_inputs(w.B, w.Hq, w.Hkv, w.Nk, w.d, torch.bfloat16, w.seed,
+                                       w.len_lo, w.len_hi, device=DEV)
+    o, lse = attn_decode(q, kc, vc, seqlens)
+    torch.cuda.synchronize()
+    sl = seqlens.cpu().numpy()
+    picks = sorted({int(np.argmin(sl)), int(np.argmax(sl)), 0, w.B - 1, 17, 40})
+    for b in picks:
+        n = int(sl[b])
+        O, L = oracle.decode(to64(q[b:b + 1]), to64(kc[b:b + 1, :n]), to64(vc[b:b + 1, :n]),
+                             np.array([n]), w.scale)
+        check(o[b:b + 1], O, lse[b:b + 1], L, where=f"full decode b={b} len={n}")
