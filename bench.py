@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--workload", default="default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="before the steps, copy this many MiB device-to-device once "
+                         "(a plain copy of known size that scales HBM byte counters)")
     return ap.parse_args()
 
 
@@ -146,6 +149,14 @@ def main():
         names = [args.workload]
     parts = [Part(n, dev) for n in names]
     torch.cuda.synchronize()
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         for p in parts:

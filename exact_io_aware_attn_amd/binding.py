@@ -22,7 +22,7 @@ MIATTN_MASK_NONE, MIATTN_MASK_CAUSAL, MIATTN_MASK_BLOCK = 0, 1, 2
 SOFTMAX_MODES = {"online": 0, "fixed_max": 1, "fixed_max_centered": 2}
 
 _EXPORTS = ("attn_fwd", "attn_fwd_workspace_bytes", "attn_decode",
-            "attn_decode_workspace_bytes", "attn_decode_chunk", "attn_status_str")
+            "attn_decode_workspace_bytes", "attn_status_str")
 
 
 class MiattnError(RuntimeError):
@@ -56,8 +56,6 @@ def library():
     lib.attn_fwd.restype = I
     lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.attn_decode_workspace_bytes.restype = Z
-    lib.attn_decode_chunk.argtypes = [I, I, I, I]
-    lib.attn_decode_chunk.restype = I
     lib.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I,
                                 ctypes.POINTER(_Strides), P, Z, P]
     lib.attn_decode.restype = I
@@ -73,12 +71,8 @@ def attn_fwd_workspace_bytes(B, Hkv, Nk, d, softmax_mode):
     return int(library().attn_fwd_workspace_bytes(B, Hkv, Nk, d, softmax_mode))
 
 
-def attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d, kv_chunk=0):
-    return int(library().attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d, kv_chunk))
-
-
-def attn_decode_chunk(B, Hkv, max_len, kv_chunk=0):
-    return int(library().attn_decode_chunk(B, Hkv, max_len, kv_chunk))
+def attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d, kv_splits=0):
+    return int(library().attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d, kv_splits))
 
 
 def _dtype_code(t):
@@ -155,7 +149,7 @@ def attn_fwd(q, k, v, *, causal=False, block_mask=None, block=None, scale=None,
     return o, lse
 
 
-def attn_decode(q, k_cache, v_cache, seqlens, *, scale=None, kv_chunk=0, return_lse=True,
+def attn_decode(q, k_cache, v_cache, seqlens, *, scale=None, kv_splits=0, return_lse=True,
                 out=None, lse_out=None, workspace=None):
     """Decode attention: q [B,Hq,d] bf16 against caches [B,max_len,Hkv,d] bf16 with
     seqlens int32 [B] (all GPU tensors). Returns (o [B,Hq,d], lse [B,Hq] or None)."""
@@ -174,13 +168,13 @@ def attn_decode(q, k_cache, v_cache, seqlens, *, scale=None, kv_chunk=0, return_
     lse = None
     if return_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse_out is None else lse_out
-    need = attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d, kv_chunk)
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d, kv_splits)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     st = (_Strides * 2)(_strides4(k_cache), _strides4(v_cache))
     rc = library().attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o),
                                _ptr(lse), _dtype_code(q), B, Hq, Hkv, max_len, d, scale,
-                               kv_chunk, st, _ptr(workspace),
+                               kv_splits, st, _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(dev))
     if rc != 0:
         raise MiattnError(rc, "attn_decode")

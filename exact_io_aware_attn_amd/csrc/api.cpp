@@ -45,28 +45,30 @@ bool strides_ok(const miattn_strides& s, int64_t mult) {
          s.h % mult == 0;
 }
 
-int decode_chunk(int B, int Hkv, int max_len, int kv_chunk) {
-  if (kv_chunk > 0) return kv_chunk;
-  // aim at ~16K (batch, KV head, chunk) work items, chunks of >= 256 keys
-  const int64_t items = (int64_t)(B > 0 ? B : 1) * (Hkv > 0 ? Hkv : 1);
-  int64_t n = (16384 + items - 1) / items;
-  const int64_t max_n = (max_len + 255) / 256;
-  if (n > max_n) n = max_n;
-  if (n < 1) n = 1;
-  int64_t c = (max_len + n - 1) / n;
-  c = (c + 63) / 64 * 64;
-  if (c < 64) c = 64;
-  return (int)c;
+// Decode partials: part_o [(kMaxSplits + B) * Hq][d] then part_lse
+// [(kMaxSplits + B) * Hq], fp32; sized for the largest split count.
+size_t decode_ws(int B, int Hq, int d) {
+  const size_t slots = (size_t)(miattn::kMaxSplits + B) * Hq;
+  return align_up(slots * d * sizeof(float)) + align_up(slots * sizeof(float));
 }
 
-// Chunking of the decode cache and the bytes of its partials: part_o
-// [B][Hq][n_chunks][d] then part_lse [B][Hq][n_chunks], both fp32.
-size_t decode_layout(int B, int Hq, int Hkv, int max_len, int d, int kv_chunk, int* chunk,
-                     int* n_chunks) {
-  *chunk = decode_chunk(B, Hkv, max_len > 0 ? max_len : 1, kv_chunk);
-  *n_chunks = max_len > 0 ? (max_len + *chunk - 1) / *chunk : 1;
-  return align_up((size_t)B * Hq * *n_chunks * d * sizeof(float)) +
-         align_up((size_t)B * Hq * *n_chunks * sizeof(float));
+// Ranges the decode cache is cut into: the caller's count, or enough
+// workgroups for every CU of the current device to hold one resident
+// workgroup's worth of waves (eight 64-lane waves per CU).
+int decode_splits(int Hkv, int kv_splits) {
+  if (kv_splits > 0) return kv_splits;
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      ncu = v;
+  }
+  const int nw = miattn::decode_waves_per_group(Hkv);
+  const int groups = Hkv / nw;
+  int n = ncu * (8 / nw) / groups;
+  if (n < 1) n = 1;
+  if (n > miattn::kMaxSplits) n = miattn::kMaxSplits;
+  return n;
 }
 
 }  // namespace
@@ -187,19 +189,16 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;
 }
 
-int attn_decode_chunk(int B, int Hkv, int max_len, int kv_chunk) {
-  return decode_chunk(B, Hkv, max_len, kv_chunk);
-}
-
-size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d, int kv_chunk) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_len < 0 || d <= 0) return 0;
-  int chunk, n_chunks;
-  return decode_layout(B, Hq, Hkv, max_len, d, kv_chunk, &chunk, &n_chunks);
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d, int kv_splits) {
+  (void)max_len;
+  (void)kv_splits;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return 0;
+  return decode_ws(B, Hq, d);
 }
 
 int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* seqlens, void* o, float* lse, int dtype, int B, int Hq, int Hkv,
-                int max_len, int d, float scale, int kv_chunk,
+                int max_len, int d, float scale, int kv_splits,
                 const miattn_strides* cache_strides, void* workspace, size_t workspace_bytes,
                 void* stream) {
   if (dtype != MIATTN_BF16) return MIATTN_ERR_UNSUPPORTED;
@@ -208,7 +207,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
   if (d != 64 && d != 128) return MIATTN_ERR_UNSUPPORTED;
   if (Hq / Hkv > 16) return MIATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(scale) || !(scale > 0.f)) return MIATTN_ERR_ARG;
-  if (kv_chunk < 0 || (kv_chunk > 0 && kv_chunk % 64 != 0)) return MIATTN_ERR_ARG;
+  if (kv_splits < 0 || kv_splits > miattn::kMaxSplits) return MIATTN_ERR_ARG;
   if (B == 0) return MIATTN_OK;
   if (q == nullptr || o == nullptr || seqlens == nullptr) return MIATTN_ERR_NULL;
   if (max_len > 0 && (k_cache == nullptr || v_cache == nullptr)) return MIATTN_ERR_NULL;
@@ -222,9 +221,8 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
   if (!strides_ok(sk, 8) || !strides_ok(sv, 8)) return MIATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return MIATTN_ERR_UNSUPPORTED;
 
-  int chunk, n_chunks;
-  const size_t need = decode_layout(B, Hq, Hkv, max_len, d, kv_chunk, &chunk, &n_chunks);
-  const size_t po = align_up((size_t)B * Hq * n_chunks * d * sizeof(float));
+  const size_t need = decode_ws(B, Hq, d);
+  const size_t po = align_up((size_t)(miattn::kMaxSplits + B) * Hq * d * sizeof(float));
   if (workspace == nullptr || workspace_bytes < need) return MIATTN_ERR_WORKSPACE;
 
   miattn::DecodeParams p{};
@@ -233,8 +231,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
   p.v_sb = sv.b; p.v_ss = sv.s; p.v_sh = sv.h;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.max_len = max_len;
   p.scale_log2 = scale * 1.4426950408889634f;
-  p.chunk = chunk;
-  p.n_chunks = n_chunks;
+  p.n_splits = decode_splits(Hkv, kv_splits);
   p.part_o = (float*)workspace;
   p.part_lse = (float*)((char*)workspace + po);
   hipError_t e = miattn::launch_decode(p, d, (hipStream_t)stream);

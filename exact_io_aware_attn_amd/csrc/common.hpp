@@ -73,6 +73,16 @@ __device__ __forceinline__ s16x4 lds_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
+// Orders this wave's earlier LDS writes before its later LDS reads of other
+// lanes' data. LDS instructions of one wave execute in order, so only the
+// compiler must be kept from reordering; no wait is emitted and, unlike
+// __syncthreads(), outstanding global loads are not waited for.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }

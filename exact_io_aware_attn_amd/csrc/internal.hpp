@@ -60,10 +60,13 @@ struct DecodeParams {
   int64_t v_sb, v_ss, v_sh;
   int B, Hq, Hkv, max_len;
   float scale_log2;
-  int chunk, n_chunks;
-  float* part_o;     // [B][Hq][n_chunks][d]
-  float* part_lse;   // [B][Hq][n_chunks]
+  int n_splits;      // ranges the flattened cache is cut into (<= kMaxSplits)
+  float* part_o;     // [n_splits + B][Hq][d], slot = range + batch
+  float* part_lse;   // [n_splits + B][Hq]
 };
+
+constexpr int kMaxSplits = 4096;
+int decode_waves_per_group(int Hkv);
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool block,
                            hipStream_t s);

@@ -113,16 +113,18 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace attn_decode needs for the split-K partials
- * (0 when the sizes are invalid). */
-size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d, int kv_chunk);
+ * (0 when the sizes are invalid). Independent of max_len and kv_splits. */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d, int kv_splits);
 
 /* Decode: one new query token per sequence against a contiguous KV cache
  * ("Role of KV Cache"; "Two Phases of Inference", Decode): query token b
  * attends to the first seqlens[b] cached keys of its sequence.
  *
- * The cache is split into chunks of kv_chunk keys; each chunk's normalised
- * output and LSE are written to the workspace and merged with the block rule
- * of "플래시어텐션..." §2 타일링 (weights exp(LSE_c - LSE)).
+ * The cached rows of all sequences, laid end to end, are cut into kv_splits
+ * equal ranges, so every workgroup streams the same number of rows whatever
+ * the length mix. Each range writes a normalised output and LSE for every
+ * sequence it touches to the workspace, and a second kernel merges them with
+ * the block rule of "플래시어텐션..." §2 타일링 (weights exp(LSE_c - LSE)).
  *
  * q        device, [B, Hq, d] bf16, packed       (read)
  * k_cache, v_cache  device, [B, max_len, Hkv, d] bf16 (read; rows at or past
@@ -133,18 +135,16 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d, i
  * lse      device, float [B, Hq] or NULL          (written)
  * dtype    MIATTN_BF16
  * d        64 or 128; Hq / Hkv <= 16
- * kv_chunk keys per split, a positive multiple of 64, or 0 for automatic
+ * kv_splits  number of ranges, 1..4096, or 0 for automatic (enough to
+ *          fill every CU of the current device)
  * cache_strides  NULL (packed) or an array of 2: k_cache, v_cache
  * workspace  device, at least attn_decode_workspace_bytes(...) bytes
  * A sequence of length 0 yields O = 0 and LSE = -inf. */
 int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* seqlens, void* o, float* lse, int dtype, int B,
-                int Hq, int Hkv, int max_len, int d, float scale, int kv_chunk,
+                int Hq, int Hkv, int max_len, int d, float scale, int kv_splits,
                 const miattn_strides* cache_strides, void* workspace,
                 size_t workspace_bytes, void* stream);
-
-/* The key chunk attn_decode uses for kv_chunk = 0 (or the value given). */
-int attn_decode_chunk(int B, int Hkv, int max_len, int kv_chunk);
 
 /* Static description of a status code. */
 const char* attn_status_str(int status);

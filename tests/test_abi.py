@@ -47,10 +47,8 @@ def test_workspace_sizes():
     centred = bd.attn_fwd_workspace_bytes(1, 24, 14080, 128, 2)
     assert plain >= 24 * 64 * 4 and centred > plain
     ws = bd.attn_decode_workspace_bytes(64, 32, 8, 32768, 128, 0)
-    chunk = bd.attn_decode_chunk(64, 8, 32768, 0)
-    n = -(-32768 // chunk)
-    assert chunk % 64 == 0 and ws >= 64 * 32 * n * 129 * 4
-    assert bd.attn_decode_chunk(64, 8, 32768, 512) == 512
+    assert ws >= (4096 + 64) * 32 * 129 * 4
+    assert ws == bd.attn_decode_workspace_bytes(64, 32, 8, 100, 128, 17)
 
 
 def _fwd(**kw):
@@ -99,7 +97,7 @@ def _dec(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=1), 3), (dict(d=80), 3), (dict(Hq=7), 2), (dict(Hq=34, Hkv=2), 3),
-    (dict(scale=-1.0), 6), (dict(chunk=100), 6), (dict(seqlens=None), 1),
+    (dict(scale=-1.0), 6), (dict(chunk=-1), 6), (dict(chunk=5000), 6), (dict(seqlens=None), 1),
     (dict(ws=None), 4), (dict(B=0), 0),
 ])
 def test_decode_validation(kw, status):

@@ -24,15 +24,34 @@ def _run(seqlens, q, kc, vc, **kw):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4), (16, 1)])
-@pytest.mark.parametrize("kv_chunk", [0, 64, 192])
-def test_decode_small(d, Hq, Hkv, kv_chunk):
+@pytest.mark.parametrize("kv_splits", [0, 1, 3, 40])
+def test_decode_small(d, Hq, Hkv, kv_splits):
     seqlens, q, kc, vc = decode_inputs(5, Hq, Hkv, 700, d, torch.bfloat16, seed=d + Hq, len_lo=1, len_hi=700)
     seqlens[0] = 700
     seqlens[1] = 1
     seqlens[2] = 64
-    o, lse = _run(seqlens, q, kc, vc, kv_chunk=kv_chunk)
+    o, lse = _run(seqlens, q, kc, vc, kv_splits=kv_splits)
     O, L = oracle.decode(to64(q), to64(kc), to64(vc), seqlens.numpy(), 1 / math.sqrt(d))
-    check(o, O, lse, L, where=f"decode d={d} H={Hq}/{Hkv} chunk={kv_chunk}")
+    check(o, O, lse, L, where=f"decode d={d} H={Hq}/{Hkv} splits={kv_splits}")
+
+
+@pytest.mark.parametrize("kv_splits", [0, 7, 2000])
+def test_decode_ragged_lengths_and_split_counts(kv_splits):
+    """Lengths around slice and range edges, zeros in between, more ranges
+    than rows (2000 > sum of lengths caps at one row per range)."""
+    lens = [0, 1, 31, 32, 33, 0, 95, 200, 0, 17]
+    seqlens, q, kc, vc = decode_inputs(len(lens), 8, 2, 200, 128, torch.bfloat16, seed=9)
+    seqlens = torch.tensor(lens, dtype=torch.int32)
+    o, lse = _run(seqlens, q, kc, vc, kv_splits=kv_splits)
+    O, L = oracle.decode(to64(q), to64(kc), to64(vc), seqlens.numpy(), 1 / math.sqrt(128))
+    check(o, O, lse, L, where=f"ragged splits={kv_splits}")
+
+
+def test_decode_all_lengths_zero():
+    seqlens, q, kc, vc = decode_inputs(3, 4, 2, 64, 64, torch.bfloat16, seed=10)
+    seqlens = torch.zeros(3, dtype=torch.int32)
+    o, lse = _run(seqlens, q, kc, vc)
+    assert (o.float() == 0).all() and torch.isneginf(lse).all()
 
 
 def test_decode_zero_length():
