@@ -139,6 +139,11 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     return MIATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(o) || !aligned16(k) || !aligned16(v))
     return MIATTN_ERR_UNSUPPORTED;
+  // rows must not overlap, and one (batch, KV head) of K or V must span less
+  // than 2 GiB (its rows are addressed with 32-bit byte offsets)
+  if (sq.s < d || sk.s < d || sv.s < d || so.s < d) return MIATTN_ERR_UNSUPPORTED;
+  if ((int64_t)Nk * sk.s * esz >= ((int64_t)1 << 31) || (int64_t)Nk * sv.s * esz >= ((int64_t)1 << 31))
+    return MIATTN_ERR_UNSUPPORTED;
 
   const size_t need = fwd_ws(B, Hkv, d, softmax_mode);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MIATTN_ERR_WORKSPACE;

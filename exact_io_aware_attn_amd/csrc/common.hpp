@@ -27,6 +27,26 @@ constexpr float kTau = 64.0f;
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// Raw buffer resource over [base, base + bytes): loads whose total offset
+// (lane offset + scalar offset) falls at or past `bytes` return 0 per dword
+// without touching memory, which zero-fills tails without branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset past any range used here
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+// HBM -> LDS without registers (buffer_load_dwordx4 ... lds): lane i's 16
+// bytes (from voff, zero when out of range) land at lds_wave + 16 * i, where
+// lds_wave is the same for the whole wave. Completion is counted by vmcnt.
+__device__ __forceinline__ void buf_load_lds16(rsrc_t r, const void* lds_wave, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)(lds_wave), 16, voff, 0, 0, 0);
+}
+
 // exp2 on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }

@@ -8,9 +8,12 @@
 //
 // Layout of the work (our design for CDNA4, not the pages' CUDA loop order):
 //  * One workgroup = 4 waves = 128 query rows of one (batch, query head); the
-//    Q tile stays in VGPRs, O accumulates in VGPRs; K/V tiles of 64 keys are
-//    streamed HBM -> VGPR -> LDS, double-buffered (the next tile's global
-//    loads are in flight while the current tile is consumed).
+//    Q tile stays in VGPRs, O accumulates in VGPRs; K/V tiles of 64 keys go
+//    HBM -> LDS directly (buffer loads into LDS, no staging registers),
+//    double-buffered in four separate LDS arrays so the next tile's loads
+//    are in flight while the current tile is consumed. Each load
+//    instruction fills 1 KiB of LDS in lane order, so every lane fetches the
+//    global 16-byte chunk that belongs in its (swizzled) LDS slot.
 //  * Each wave owns 32 query rows and computes S^T = K Q^T with
 //    v_mfma_f32_32x32x16_bf16, so every lane holds the scores of ONE query
 //    for 16 keys of a 32-key block: the row max needs one cross-lane step
@@ -23,12 +26,20 @@
 //    applied only on tiles that cross the diagonal. Block mask: the workgroup
 //    walks only the union of its rows' live key blocks; a wave whose rows all
 //    share that live set applies no mask at all (blocks are never partial).
+//  * The softmax scale is folded into the exponent argument (one FMA per
+//    score: exp2(s * scale*log2(e) - m)), and the running max is used lazily:
+//    the reference max m of a row moves only when a tile's max exceeds it by
+//    more than kRescaleThr (log2 units), so the O rescale runs on few tiles
+//    and P stays below 2^kRescaleThr. Any reference gives the same exact
+//    result; the final division by l uses the same reference.
 //  * Fixed-max softmax (TPU attention guide, 4단계): the per-row bound
 //    M_i = scale*|q_i|*rho replaces the running max, removing the max
 //    reduction and the accumulator rescale; a 32-row group whose bound is too
 //    loose falls back to the running max.
 //  * Workgroup order: heaviest causal tiles first; the query heads sharing a
 //    KV head land on the same XCD (blockIdx % 8) so K/V are reused in its L2.
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -40,6 +51,7 @@ namespace {
 constexpr int BQ = 128;  // query rows per workgroup
 constexpr int BK = 64;   // keys per tile
 constexpr int NT = 256;  // threads per workgroup
+constexpr float kRescaleThr = 8.f;  // lazy rescale threshold, log2 units
 
 // LDS swizzles on 16-byte chunks, chosen so the MFMA-side reads hit distinct
 // banks: K is read 16 rows x one chunk per 16 lanes; V is read by the
@@ -78,18 +90,20 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   constexpr int CH = D / 8;          // 16-byte chunks per K/V row
   constexpr int KSTEPS = D / 16;     // k-steps of the S^T MFMA
   constexpr int MB = D / 32;         // 32-row blocks of O^T
-  constexpr int RPP = NT / CH;       // tile rows staged per pass
-  constexpr int NPASS = BK / RPP;    // staging passes per tile
+  constexpr int RPI = 1024 / (D * 2);  // tile rows per 1 KiB load instruction
+  constexpr int NIW = BK / RPI / 4;    // load instructions per wave per tile
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2 * BK * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2 * BK * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sK0[BK * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sK1[BK * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV0[BK * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV1[BK * D];
   __shared__ short sLive[BLOCK ? kMaxLiveBlocks : 1];
   __shared__ int sCount;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int c = lane & 31;  // query column of this lane
+  const int qc = lane & 31;  // query column of this lane
   const int h = lane >> 5;  // which half of each 8-row group of keys
 
   const int G = p.Hq / p.Hkv;
@@ -105,7 +119,7 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   const int q_start = qt * BQ;
   const int q_end = min(q_start + BQ, p.Nq);
   const int q0 = q_start + wave * 32;
-  const int qrow = q0 + c;
+  const int qrow = q0 + qc;
   const bool row_ok = qrow < p.Nq;
   const int wave_last = min(q0 + 31, p.Nq - 1);  // last valid row of the wave
 
@@ -202,36 +216,56 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     fixed = wave_max(gap) <= kTau;
   }
 
-  // ---- staging of one K/V tile: thread -> (row r, chunk ch)
-  u32x4 kreg[NPASS], vreg[NPASS];
-  const int st_row = tid / CH;
-  const int st_ch = tid - st_row * CH;
-  auto load_tile = [&](int t) {
+  // ---- staging: instruction j of this wave fills tile rows
+  // r = (wave*NIW + j)*RPI + lane/CH, LDS slot lane%CH of the row, which holds
+  // the logical chunk kswz(r, slot) (the swizzles are involutions).
+  const int dma_row0 = wave * NIW * RPI + lane / CH;
+  const int dma_slot = lane % CH;
+  uint32_t dko[NIW], dvo[NIW];  // byte offsets within a tile (dense path)
 #pragma unroll
-    for (int i = 0; i < NPASS; ++i) {
-      const int r = st_row + RPP * i;
-      int key;
-      bool ok;
-      if constexpr (!BLOCK) {
-        key = t * BK + r;
-        ok = key < kv_end;
-      } else {
-        const int L = t * BK + r;
-        ok = L < n_live_keys;
-        const int blk = ok ? L / p.block_k : 0;
-        key = ok ? (int)sLive[blk] * p.block_k + (L - blk * p.block_k) : 0;
-      }
-      u32x4 z = {0u, 0u, 0u, 0u};
-      kreg[i] = ok ? *(const u32x4*)(kg + (int64_t)key * p.k_ss + st_ch * 8) : z;
-      vreg[i] = ok ? *(const u32x4*)(vg + (int64_t)key * p.v_ss + st_ch * 8) : z;
-    }
+  for (int j = 0; j < NIW; ++j) {
+    const int r = dma_row0 + j * RPI;
+    dko[j] = (uint32_t)(r * p.k_ss + kswz<D>(r, dma_slot) * 8) * 2u;
+    dvo[j] = (uint32_t)(r * p.v_ss + vswz<D>(r, dma_slot) * 8) * 2u;
+  }
+  // bytes covering rows [0, n) of a [rows, stride] view with d elements per row
+  auto span = [](int n, int64_t stride) -> uint32_t {
+    return n > 0 ? (uint32_t)(((int64_t)(n - 1) * stride + D) * 2) : 0u;
   };
-  auto store_tile = [&](int buf) {
+  // BLOCK: one resource over all Nk rows, rows gathered by key index
+  const rsrc_t rk_all = make_rsrc(kg, span(p.Nk, p.k_ss));
+  const rsrc_t rv_all = make_rsrc(vg, span(p.Nk, p.v_ss));
+  auto issue_tile = [&](int t, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    __bf16* const dk = BUF ? sK1 : sK0;
+    __bf16* const dv = BUF ? sV1 : sV0;
+    if constexpr (!BLOCK) {
+      const int r0 = t * BK;
+      const int nvalid = min(BK, kv_end - r0);
+      const rsrc_t rk = make_rsrc(kg + (int64_t)r0 * p.k_ss, span(nvalid, p.k_ss));
+      const rsrc_t rv = make_rsrc(vg + (int64_t)r0 * p.v_ss, span(nvalid, p.v_ss));
 #pragma unroll
-    for (int i = 0; i < NPASS; ++i) {
-      const int r = st_row + RPP * i;
-      *(u32x4*)(sK + buf * BK * D + r * D + kswz<D>(r, st_ch) * 8) = kreg[i];
-      *(u32x4*)(sV + buf * BK * D + r * D + vswz<D>(r, st_ch) * 8) = vreg[i];
+      for (int j = 0; j < NIW; ++j) {
+        const int lds_row = (wave * NIW + j) * RPI;
+        buf_load_lds16(rk, dk + lds_row * D, dko[j]);
+        buf_load_lds16(rv, dv + lds_row * D, dvo[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NIW; ++j) {
+        const int r = dma_row0 + j * RPI;
+        const int L = t * BK + r;
+        uint32_t ko = kOutOfRange, vo = kOutOfRange;
+        if (L < n_live_keys) {
+          const int blk = L / p.block_k;
+          const int key = (int)sLive[blk] * p.block_k + (L - blk * p.block_k);
+          ko = (uint32_t)(key * p.k_ss + kswz<D>(r, dma_slot) * 8) * 2u;
+          vo = (uint32_t)(key * p.v_ss + vswz<D>(r, dma_slot) * 8) * 2u;
+        }
+        const int lds_row = (wave * NIW + j) * RPI;
+        buf_load_lds16(rk_all, dk + lds_row * D, ko);
+        buf_load_lds16(rv_all, dv + lds_row * D, vo);
+      }
     }
   };
 
@@ -241,24 +275,20 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[mb][r] = 0.f;
-  float m_run = kNegInf;  // running max (log2 units), online mode
+  float m_run = kNegInf;  // reference max (log2 units), online mode
   float l_run = 0.f;      // this lane's partial row sum (half of the keys)
+  const float c = p.scale_log2;
 
   // per-lane address pieces for the V^T transpose reads (see PV below)
   const int tr_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int tr_ch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int tr_half = 4 * (lane & 1);
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
-
+  // one tile of keys from LDS buffer BUF (compile-time)
+  auto tile_body = [&](int t, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    const __bf16* const sk = BUF ? sK1 : sK0;
+    const __bf16* const sv = BUF ? sV1 : sV0;
     // ---- what this wave has to do with this tile
     // state 0: nothing visible, 1: everything visible, 2: apply the mask
     int state = 1;
@@ -293,25 +323,31 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
     if (state != 0) {
       // ---- S^T = K Q^T for two 32-key blocks
       f32x16 s[2];
-      const __bf16* sk = sK + buf * BK * D;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-        const int row = 32 * kb + c;
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          const bf16x8 kf = *(const bf16x8*)(sk + row * D + kswz<D>(row, 2 * ks + h) * 8);
-          s[kb] = mfma32(kf, qf[ks], s[kb]);
-        }
-      }
-
-      // ---- scale to log2 units and mask. Lane (c, h), register r of block
-      // kb holds key 32kb + 8(r/4) + 4h + r%4 of the tile, query qrow.
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] *= p.scale_log2;
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      // K fragment of block kb, k-step ks: row 32kb + qc, chunk 2ks + h
+      auto kfrag = [&](int kb, int ks) {
+        const int row = 32 * kb + qc;
+        return *(const bf16x8*)(sk + row * D + kswz<D>(row, 2 * ks + h) * 8);
+      };
+      bf16x8 ka = kfrag(0, 0), kc = kfrag(1, 0);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        bf16x8 na = ka, nc = kc;
+        if (ks + 1 < KSTEPS) {
+          na = kfrag(0, ks + 1);
+          nc = kfrag(1, ks + 1);
+        }
+        s[0] = mfma32(ka, qf[ks], s[0]);
+        s[1] = mfma32(kc, qf[ks], s[1]);
+        ka = na;
+        kc = nc;
+      }
+
+      // ---- mask (raw scores). Lane (qc, h), register r of block kb holds
+      // key 32kb + 8(r/4) + 4h + r%4 of the tile, query qrow.
       if (state == 2) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -336,48 +372,51 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
           }
       }
 
-      // ---- softmax update
+      // ---- softmax update: p = exp2(s * c - m), one FMA + one exp per score
+      float m_use;
       if (!fixed) {
         float mx = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == kNegInf ? 0.f : m_new;
-        const float alpha = ex2(m_run - m_use);
-        m_run = m_new;
-        if (__ballot(alpha != 1.f)) {
+        mx = fmaxf(mx, shfl_xor(mx, 32)) * c;  // tile max of the row, log2 units
+        if (__ballot(mx > m_run + kRescaleThr)) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = ex2(m_run - (m_new == kNegInf ? 0.f : m_new));
+          m_run = m_new;
           l_run *= alpha;
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
         }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = ex2(s[kb][r] - m_use);
-            s[kb][r] = e;
-            l_run += e;
-          }
+        m_use = m_run == kNegInf ? 0.f : m_run;
       } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = ex2(s[kb][r] - m_fix);
-            s[kb][r] = e;
-            l_run += e;
-          }
+        m_use = m_fix;
       }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = ex2(__builtin_fmaf(s[kb][r], c, -m_use));
+          s[kb][r] = e;
+          l_run += e;
+        }
 
       // ---- O^T += V^T P^T, four 16-key steps. Step u uses registers
       // 8(u%2) .. +7 of block u/2: keys 16u + 4h + e (e < 4) and
       // 16u + 8 + 4h + (e - 4) (e >= 4) for query c -- the B operand as is.
-      const __bf16* sv = sV + buf * BK * D;
+      // A operand of step u, block mb (V^T rows 32mb..+31, the step's 16
+      // keys): two transpose reads, keys 16u + 8rr + 4h' + j of the groups
+      auto vfrag = [&](int u, int mb) {
+        const int ch = 4 * mb + tr_ch;
+        const int r0 = 16 * u + tr_row, r1 = 16 * u + 8 + tr_row;
+        const s16x4 lo = lds_tr16(sv + r0 * D + vswz<D>(r0, ch) * 8 + tr_half);
+        const s16x4 hi = lds_tr16(sv + r1 * D + vswz<D>(r1, ch) * 8 + tr_half);
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 vcur = vfrag(0, 0);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const f32x16& sb = s[u >> 1];
@@ -386,27 +425,27 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
                                sb[o8 + 5], sb[o8 + 6], sb[o8 + 7]);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          // A operand (V^T rows 32mb..+31, the same 16 keys): two transpose
-          // reads, keys 16u + 8rr + 4h' + j for the lanes' groups.
-          s16x4 lo, hi;
-          {
-            const int row = 16 * u + tr_row;
-            const int ch = 4 * mb + tr_ch;
-            lo = lds_tr16(sv + row * D + vswz<D>(row, ch) * 8 + tr_half);
-          }
-          {
-            const int row = 16 * u + 8 + tr_row;
-            const int ch = 4 * mb + tr_ch;
-            hi = lds_tr16(sv + row * D + vswz<D>(row, ch) * 8 + tr_half);
-          }
-          const s16x8 a16 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[mb] = mfma32(__builtin_bit_cast(bf16x8, a16), pf, oacc[mb]);
+          const int nxt = u * MB + mb + 1;
+          bf16x8 vnext = vcur;
+          if (nxt < 4 * MB) vnext = vfrag(nxt / MB, nxt % MB);
+          oacc[mb] = mfma32(vcur, pf, oacc[mb]);
+          vcur = vnext;
         }
       }
     }
+  };
 
-    if (t + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
+  if (n_tiles > 0) issue_tile(0, std::integral_constant<int, 0>());
+  __syncthreads();
+  for (int t = 0; t < n_tiles; t += 2) {
+    if (t + 1 < n_tiles) issue_tile(t + 1, std::integral_constant<int, 1>());
+    tile_body(t, std::integral_constant<int, 0>());
+    __syncthreads();  // buffer 0 free; tile t+1 landed in buffer 1
+    if (t + 1 < n_tiles) {
+      if (t + 2 < n_tiles) issue_tile(t + 2, std::integral_constant<int, 0>());
+      tile_body(t + 1, std::integral_constant<int, 1>());
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2
