@@ -7,7 +7,8 @@
 // "FlashAttention / Tiling" and "Online-Softmax").
 //
 // Layout of the work (our design for CDNA4, not the pages' CUDA loop order):
-//  * One workgroup = 4 waves = 128 query rows of one (batch, query head); the
+//  * One workgroup = 4 or 8 waves = 128 or 256 query rows of one (batch,
+//    query head) (8 when the problem still yields >= 1024 workgroups); the
 //    Q tile stays in VGPRs, O accumulates in VGPRs; K/V tiles of 64 keys go
 //    HBM -> LDS directly (buffer loads into LDS, no staging registers),
 //    double-buffered in four separate LDS arrays so the next tile's loads
@@ -48,9 +49,7 @@ namespace miattn {
 
 namespace {
 
-constexpr int BQ = 128;  // query rows per workgroup
 constexpr int BK = 64;   // keys per tile
-constexpr int NT = 256;  // threads per workgroup
 constexpr float kRescaleThr = 8.f;  // lazy rescale threshold, log2 units
 
 // LDS swizzles on 16-byte chunks, chosen so the MFMA-side reads hit distinct
@@ -85,13 +84,15 @@ __device__ __forceinline__ void map_workgroup(int i, int G, int nX, int& X, int&
   }
 }
 
-template <int D, bool CAUSAL, bool BLOCK>
-__global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
+// NW waves per workgroup (4 or 8), 32 query rows per wave
+template <int D, bool CAUSAL, bool BLOCK, int NW>
+__global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdParams p) {
+  constexpr int BQ = 32 * NW;        // query rows per workgroup
   constexpr int CH = D / 8;          // 16-byte chunks per K/V row
   constexpr int KSTEPS = D / 16;     // k-steps of the S^T MFMA
   constexpr int MB = D / 32;         // 32-row blocks of O^T
   constexpr int RPI = 1024 / (D * 2);  // tile rows per 1 KiB load instruction
-  constexpr int NIW = BK / RPI / 4;    // load instructions per wave per tile
+  constexpr int NIW = BK / RPI / NW;   // load instructions per wave per tile
 
   __shared__ __attribute__((aligned(16))) __bf16 sK0[BK * D];
   __shared__ __attribute__((aligned(16))) __bf16 sK1[BK * D];
@@ -470,18 +471,27 @@ __global__ void __launch_bounds__(NT, 2) fwd_bf16_kernel(const FwdParams p) {
 }
 
 template <int D, bool CAUSAL, bool BLOCK>
-hipError_t launch_one(const FwdParams& p, hipStream_t s) {
-  const int grid = p.n_qtiles * p.B * p.Hq;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BLOCK>), dim3(grid), dim3(NT), 0, s, p);
+hipError_t launch_one(const FwdParams& p0, hipStream_t s) {
+  // 8 waves (256 rows) per workgroup share each K/V tile when that still
+  // leaves >= 1024 workgroups; smaller problems use 4 waves (128 rows)
+  FwdParams p = p0;
+  const int64_t big = (int64_t)((p.Nq + 255) / 256) * p.B * p.Hq;
+  if (big >= 1024) {
+    p.n_qtiles = (p.Nq + 255) / 256;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BLOCK, 8>), dim3(p.n_qtiles * p.B * p.Hq),
+                       dim3(512), 0, s, p);
+  } else {
+    p.n_qtiles = (p.Nq + 127) / 128;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BLOCK, 4>), dim3(p.n_qtiles * p.B * p.Hq),
+                       dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdParams& p0, int d, bool causal, bool block, hipStream_t s) {
-  FwdParams p = p0;
-  p.n_qtiles = (p.Nq + BQ - 1) / BQ;
-  if (p.n_qtiles == 0 || p.B == 0) return hipSuccess;
+hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool block, hipStream_t s) {
+  if (p.Nq == 0 || p.B == 0) return hipSuccess;
 #define MIATTN_DISPATCH(DD)                                                     \
   if (causal && block) return launch_one<DD, true, true>(p, s);                \
   if (causal) return launch_one<DD, true, false>(p, s);                        \

@@ -63,6 +63,32 @@ def test_bf16_shapes(d, causal, Hq, Hkv, Nq, Nk):
     check(o, O, lse, L, where=f"bf16 d={d} causal={causal} H={Hq}/{Hkv} N={Nq}x{Nk}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_eight_wave_workgroups_ragged(d, causal):
+    """Enough (batch, head) pairs that the 256-row, 8-wave workgroups are used
+    (>= 1024 of them), with ragged query and key tails and GQA."""
+    B, Hq, Hkv, Nq, Nk = 32, 16, 4, 300, 333
+    q, k, v = prefill_inputs(B, Hq, Hkv, Nq, Nk, d, torch.bfloat16, seed=d + causal)
+    o, lse = _run(q, k, v, causal=causal)
+    heads = [0, 7, 15]
+    O, L = _ref(q, k, v, 1 / math.sqrt(d), causal=causal, heads=heads)
+    check(o[:, :, heads], O, lse[:, heads], L, where=f"8-wave d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("mode", ["online", "fixed_max"])
+def test_bf16_eight_wave_frame_mask(mode):
+    frames, flen, blk = 5, 128, 64
+    n = frames * flen
+    bm = frame_block_mask(frames, flen, blk)
+    q, k, v = prefill_inputs(16, 32, 32, n, n, 128, torch.bfloat16, seed=21)
+    o, lse = _run(q, k, v, block_mask=bm, block=(blk, blk), softmax=mode)
+    heads = [0, 31]
+    O, L = _ref(q[:2], k[:2], v[:2], 1 / math.sqrt(128), block_mask=bm, block_q=blk, block_k=blk,
+                heads=heads)
+    check(o[:2][:, :, heads], O, lse[:2][:, heads], L, where=f"8-wave frames {mode}")
+
+
 @pytest.mark.parametrize("mode", ["fixed_max", "fixed_max_centered"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bf16_fixed_max(mode, causal):
