@@ -36,6 +36,29 @@ MFMA_BF16_PEAK = 2516.6   # TFLOP/s, 256 CU x 4096 FLOP/clk x 2.4 GHz (dense)
 FP32_PEAK = 157.3         # TFLOP/s
 HBM_PEAK = 8000.0         # GB/s
 
+# Counter-derived HBM bytes per launch of the kernels timed by the default step
+# (rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain
+# device copy of known size). They describe the kernel sources whose hash is
+# stored with them and are reported only while those sources are unchanged.
+DEFAULT = ("llama3-8b-gqa-causal-8k", "gqa-decode-b64")   # the default step
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def measured_traffic(part):
+    """HBM bytes per launch for this kernel from the stored counters, or None."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[part]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        with open(os.path.join(ROOT, "exact_io_aware_attn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != rec["source_sha256_16"]:
+        return None
+    return rec["bytes"]
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -144,7 +167,7 @@ def main():
     torch.cuda.set_device(0)
 
     if args.workload == "default":
-        names = ["llama3-8b-gqa-causal-8k", "gqa-decode-b64"]
+        names = list(DEFAULT)
     else:
         names = [args.workload]
     parts = [Part(n, dev) for n in names]
@@ -195,12 +218,14 @@ def main():
         peak = MFMA_BF16_PEAK if main_p.w.dtype == "bf16" else FP32_PEAK
         out.update(value=tflops, unit="TFLOP/s")
         roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
-                "frac": tflops / peak, "traffic": None}
+                "frac": tflops / peak,
+                "traffic": measured_traffic("prefill") if main_p.name == DEFAULT[0] else None}
     else:
         gbs = main_p.bytes / (ms_avg[0] * 1e-3) / 1e9
         out.update(value=gbs, unit="GB/s")
         roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK, "unit": "GB/s",
-                "frac": gbs / HBM_PEAK, "traffic": None}
+                "frac": gbs / HBM_PEAK,
+                "traffic": measured_traffic("decode") if main_p.name == DEFAULT[1] else None}
     out.update(n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=ms_step,
                higher_is_better=True, scaling="weak", vs_baseline=None,
                dtype="bf16" if main_p.w.dtype == "bf16" else "f32",
@@ -219,7 +244,8 @@ def main():
         gbs = d.bytes / (ms_avg[1] * 1e-3) / 1e9
         out["decode"] = {"value": gbs, "unit": "GB/s", "ms": ms_avg[1]}
         out["roofline_decode"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK,
-                                  "unit": "GB/s", "frac": gbs / HBM_PEAK, "traffic": None}
+                                  "unit": "GB/s", "frac": gbs / HBM_PEAK,
+                                  "traffic": measured_traffic("decode")}
     if not args.no_cpu_baseline and main_p.kind == "prefill":
         out["cpu_baseline"] = cpu_baseline(main_p, args.cpu_seconds)
     else:
