@@ -224,6 +224,10 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
     sv = cache_strides[1];
   }
   if (!strides_ok(sk, 8) || !strides_ok(sv, 8)) return MIATTN_ERR_UNSUPPORTED;
+  // one (sequence, KV head) of the cache is addressed with 32-bit byte offsets
+  if ((int64_t)max_len * sk.s * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)max_len * sv.s * 2 >= ((int64_t)1 << 31))
+    return MIATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return MIATTN_ERR_UNSUPPORTED;
 
   const size_t need = decode_ws(B, Hq, d);

@@ -14,11 +14,15 @@
 //    serves all G = Hq/Hkv query heads of its KV head, so each cache byte is
 //    read once, and the waves walk the same cache rows together, so the rows
 //    ([Hkv, d] contiguous per key) stream whole;
-//  * each wave streams 32-key slices: K goes from global memory straight into
-//    MFMA A-operand registers (16-byte loads), V is staged through an LDS
-//    slice private to the wave and read back transposed (ds_read_b64_tr_b16)
-//    for O^T = V^T P^T; the next slice's loads are in flight while the
-//    current one is consumed, and no workgroup barrier sits in the key loop;
+//  * each wave streams 32-key slices. Every load instruction reads whole
+//    rows of its KV head (16 lanes x 16 bytes per 256-byte row), so each
+//    cache line is fetched by one instruction and the loads can carry the
+//    nontemporal hint (the cache is read once). K and V land in registers,
+//    are written to an LDS slice private to the wave and read back in the
+//    MFMA operand layouts (K: 16-byte reads; V: transposed,
+//    ds_read_b64_tr_b16, for O^T = V^T P^T); the next slice's loads are in
+//    flight while the current one is consumed, and no workgroup barrier sits
+//    in the key loop;
 //  * S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16 with the
 //    query heads of the group as the 16-wide N dimension (zero-padded);
 //  * rows at or past seqlens[b] are never read;
@@ -58,13 +62,17 @@ __device__ int64_t wave_sum_lens(const int32_t* seqlens, int n, int lane) {
 
 // NW: waves per workgroup = KV heads per workgroup (a divisor of Hkv)
 template <int D, int NW>
-__global__ void __launch_bounds__(NW * 64) decode_split_kernel(const DecodeParams p) {
+__global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) decode_split_kernel(const DecodeParams p) {
   constexpr int KST = D / 32;  // k-steps (32 d each) of S^T
   constexpr int MB = D / 16;   // 16-row blocks of O^T
   constexpr int VCH = D / 8;   // 16-byte chunks per row
-  // per-wave V slice, row-major [SL][D] bf16, 16-byte chunks swizzled so the
-  // transpose reads of 4 rows x 2 chunks hit distinct banks. One buffer per
-  // wave suffices: a wave's LDS instructions execute in order.
+  constexpr int RPL = 64 / VCH;  // cache rows per load instruction
+  constexpr int NL = SL / RPL;   // load instructions per slice, K and V each
+  // per-wave K and V slices, row-major [SL][D] bf16 with 16-byte chunks
+  // swizzled (K: the 16 rows of an operand read hit distinct banks; V: the
+  // transpose reads of 4 rows x 2 chunks do). One buffer per wave suffices: a
+  // wave's LDS instructions execute in order.
+  __shared__ __attribute__((aligned(16))) __bf16 sKall[NW * SL * D];
   __shared__ __attribute__((aligned(16))) __bf16 sVall[NW * SL * D];
 
   const int lane = threadIdx.x & 63;
@@ -73,6 +81,7 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(const DecodeParam
   const int g4 = lane >> 4;   // lane group
   const int hkv = blockIdx.y * NW + wave;
   const int G = p.Hq / p.Hkv;
+  __bf16* const sk = sKall + wave * SL * D;
   __bf16* const sv = sVall + wave * SL * D;
 
   const int64_t T = wave_sum_lens(p.seqlens, p.B, lane);
@@ -85,12 +94,13 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(const DecodeParam
   const __bf16* __restrict__ kbase = (const __bf16*)p.kc + hkv * p.k_sh;
   const __bf16* __restrict__ vbase = (const __bf16*)p.vc + hkv * p.v_sh;
   auto vsw = [](int r, int ch) { return ch ^ ((r & 3) << 1); };
+  auto ksw = [](int r, int ch) { return D == 128 ? (ch ^ (r & 15)) : (ch ^ ((r >> 1) & 7)); };
   // transpose-read addressing (see common.hpp): source lane s supplies
   // row 4*(s>>4) + ((s&15)>>2) (+16 for the second read), d 16mb + 4*(s&3)
   const int tr_row = 4 * g4 + ((lane & 15) >> 2);
   const int tr_d = 4 * (lane & 3);
-  const int vrow = lane >> 1;                 // V row staged by this lane
-  const int vch0 = (lane & 1) * (VCH / 2);    // its first 16-byte chunk
+  const int lrow = lane / VCH;   // row (within a load instruction's rows) of this lane
+  const int lch = lane % VCH;    // its 16-byte chunk
 
   // walk the sequences in order; [start, start + len) is sequence b's rows
   int64_t start = 0;
@@ -100,8 +110,8 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(const DecodeParam
     if (len > 0 && end > lo) {
       const int k_begin = (int)((lo > start ? lo : start) - start);
       const int k_end = (int)((hi < end ? hi : end) - start);
-      const __bf16* kg = kbase + b * p.k_sb;
-      const __bf16* vg = vbase + b * p.v_sb;
+      const __bf16* kg = kbase + b * p.k_sb + lch * 8;
+      const __bf16* vg = vbase + b * p.v_sb + lch * 8;
 
       // Q^T as B operand: lane (n, g4), k-step t holds q[head n][32t + 8g4 .. +8]
       bf16x8 qf[KST];
@@ -117,30 +127,18 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(const DecodeParam
       }
 
       const int n_iter = (k_end - k_begin + SL - 1) / SL;
-      // K A-operand registers: slice row 16*mb2 + (lane&15), d 8*g4 + 32t
-      bf16x8 kreg[2][2][KST];
-      u32x4 vreg[2][VCH / 2];
+      // load instruction i of a slice: rows RPL*i + lrow, chunk lch
+      u32x4 kreg[2][NL], vreg[2][NL];
       auto load_set = [&](int it, auto setc) {
         constexpr int set = decltype(setc)::value;
-        const int s0 = k_begin + it * SL;
+        const int s0 = k_begin + it * SL + lrow;
 #pragma unroll
-        for (int mb2 = 0; mb2 < 2; ++mb2) {
-          const int key = s0 + 16 * mb2 + (lane & 15);
+        for (int i = 0; i < NL; ++i) {
+          const int key = s0 + RPL * i;
           const bool ok = key < k_end;
-          const __bf16* kp = kg + (int64_t)key * p.k_ss + 8 * g4;
-#pragma unroll
-          for (int t = 0; t < KST; ++t) {
-            bf16x8 z = {};
-            kreg[set][mb2][t] = ok ? *(const bf16x8*)(kp + 32 * t) : z;
-          }
-        }
-        const int key = s0 + vrow;
-        const bool ok = key < k_end;
-        const __bf16* vp = vg + (int64_t)key * p.v_ss + vch0 * 8;
-#pragma unroll
-        for (int i = 0; i < VCH / 2; ++i) {
           u32x4 z = {0u, 0u, 0u, 0u};
-          vreg[set][i] = ok ? *(const u32x4*)(vp + 8 * i) : z;
+          kreg[set][i] = ok ? __builtin_nontemporal_load((const u32x4*)(kg + (int64_t)key * p.k_ss)) : z;
+          vreg[set][i] = ok ? __builtin_nontemporal_load((const u32x4*)(vg + (int64_t)key * p.v_ss)) : z;
         }
       };
 
@@ -155,8 +153,11 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(const DecodeParam
       auto step = [&](int it, auto setc) {
         constexpr int SET = decltype(setc)::value;
 #pragma unroll
-        for (int i = 0; i < VCH / 2; ++i)
-          *(u32x4*)(sv + vrow * D + vsw(vrow, vch0 + i) * 8) = vreg[SET][i];
+        for (int i = 0; i < NL; ++i) {
+          const int r = RPL * i + lrow;
+          *(u32x4*)(sk + r * D + ksw(r, lch) * 8) = kreg[SET][i];
+          *(u32x4*)(sv + r * D + vsw(r, lch) * 8) = vreg[SET][i];
+        }
         if (it + 1 < n_iter) load_set(it + 1, std::integral_constant<int, 1 - SET>());
         wave_lds_sync();
 
@@ -165,8 +166,13 @@ __global__ void __launch_bounds__(NW * 64) decode_split_kernel(const DecodeParam
 #pragma unroll
         for (int mb2 = 0; mb2 < 2; ++mb2) {
           s[mb2] = f32x4{0.f, 0.f, 0.f, 0.f};
+          // K A operand: slice row 16mb2 + (lane&15), d 32t + 8g4 .. +8
+          const int r = 16 * mb2 + (lane & 15);
 #pragma unroll
-          for (int t = 0; t < KST; ++t) s[mb2] = mfma16k32(kreg[SET][mb2][t], qf[t], s[mb2]);
+          for (int t = 0; t < KST; ++t) {
+            const bf16x8 ka = *(const bf16x8*)(sk + r * D + ksw(r, 4 * t + g4) * 8);
+            s[mb2] = mfma16k32(ka, qf[t], s[mb2]);
+          }
         }
         // lane (n, g4), register r of half mb2: key s0 + 16mb2 + 4g4 + r, head n
         float mx = kNegInf;

@@ -99,6 +99,8 @@ def _dec(**kw):
     (dict(dtype=1), 3), (dict(d=80), 3), (dict(Hq=7), 2), (dict(Hq=34, Hkv=2), 3),
     (dict(scale=-1.0), 6), (dict(chunk=-1), 6), (dict(chunk=5000), 6), (dict(seqlens=None), 1),
     (dict(ws=None), 4), (dict(B=0), 0),
+    # one (sequence, KV head) of the cache must span < 2 GiB (32-bit offsets)
+    (dict(max_len=1 << 23), 3),
 ])
 def test_decode_validation(kw, status):
     assert _dec(**kw) == status
