@@ -25,8 +25,11 @@
 //    ds_read_b64_tr_b16, so V is never transposed in memory.
 //  * Causal: tiles wholly above a wave's rows are skipped, the element rule is
 //    applied only on tiles that cross the diagonal. Block mask: the workgroup
-//    walks only the union of its rows' live key blocks; a wave whose rows all
-//    share that live set applies no mask at all (blocks are never partial).
+//    walks only the union of its rows' live key blocks; every wave lies in
+//    one block row (rows are cut into 32-row segments of single block rows
+//    when block_q is not a multiple of 32), so a 16-key group is live or dead
+//    for the whole wave: dead groups are masked in S and skipped in PV, and a
+//    wave whose block row sees the whole union applies no mask at all.
 //  * The softmax scale is folded into the exponent argument (one FMA per
 //    score: exp2(s * scale*log2(e) - m)), and the running max is used lazily:
 //    the reference max m of a row moves only when a tile's max exceeds it by
@@ -117,12 +120,31 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
   const int qt = CAUSAL ? (p.n_qtiles - 1 - qt_rank) : qt_rank;
   const int hq = hkv * G + g;
 
-  const int q_start = qt * BQ;
-  const int q_end = min(q_start + BQ, p.Nq);
-  const int q0 = q_start + wave * 32;
+  // ---- rows of this wave. A block mask whose block_q is not a multiple of 32
+  // cuts the rows into segments that never cross a block row (32, 32, ...,
+  // the rest, per block row; lanes past a short segment hold no query), so
+  // every wave lies in one block row and can skip the key groups dead for it
+  // outright: a dead key is then never multiplied into any of the wave's rows.
+  int q_start, q_end, q0, nrows;
+  if (BLOCK && p.block_q % 32 != 0) {
+    const int spb = (p.block_q + 31) / 32;  // segments per block row
+    const int nseg = (p.Nq / p.block_q) * spb;
+    const int s0 = qt * NW, sw = s0 + wave;
+    const int brow = sw / spb;
+    q0 = sw < nseg ? brow * p.block_q + (sw - brow * spb) * 32 : p.Nq;
+    nrows = sw < nseg ? min(32, p.block_q - (sw - brow * spb) * 32) : 0;
+    const int s1 = min(s0 + NW, nseg) - 1;  // last segment of the workgroup
+    q_start = (s0 / spb) * p.block_q;
+    q_end = min(p.Nq, (s1 / spb + 1) * p.block_q);
+  } else {
+    q_start = qt * BQ;
+    q_end = min(q_start + BQ, p.Nq);
+    q0 = q_start + wave * 32;
+    nrows = 32;
+  }
   const int qrow = q0 + qc;
-  const bool row_ok = qrow < p.Nq;
-  const int wave_last = min(q0 + 31, p.Nq - 1);  // last valid row of the wave
+  const bool row_ok = qc < nrows && qrow < p.Nq;
+  const int wave_last = min(q0 + nrows - 1, p.Nq - 1);  // last valid row of the wave
 
   const __bf16* __restrict__ qg = (const __bf16*)p.q;
   const __bf16* __restrict__ kg = (const __bf16*)p.k + b * p.k_sb + hkv * p.k_sh;
@@ -310,7 +332,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
         for (int gi = 0; gi < 4; ++gi) {
           const int L = tile_k0 + 16 * gi;
           bool live = false;
-          if (L < n_live_keys && row_ok)
+          if (L < n_live_keys)  // the same for every lane: one block row per wave
             live = p.block_mask[(int64_t)my_qb * p.nkb + sLive[L / p.block_k]] != 0;
           grp_live[gi] = live;
           any |= live;
@@ -417,6 +439,21 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
         const s16x4 hi = lds_tr16(sv + r1 * D + vswz<D>(r1, ch) * 8 + tr_half);
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
+      if constexpr (BLOCK) {
+        // key group u is live or dead for the whole wave (one block row):
+        // dead groups are skipped, so their V rows never meet the wave's P
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (!grp_live[u]) continue;
+          const f32x16& sb = s[u >> 1];
+          const int o8 = 8 * (u & 1);
+          const bf16x8 pf = cvt8(sb[o8 + 0], sb[o8 + 1], sb[o8 + 2], sb[o8 + 3], sb[o8 + 4],
+                                 sb[o8 + 5], sb[o8 + 6], sb[o8 + 7]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) oacc[mb] = mfma32(vfrag(u, mb), pf, oacc[mb]);
+        }
+        return;
+      }
       bf16x8 vcur = vfrag(0, 0);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -476,12 +513,16 @@ hipError_t launch_one(const FwdParams& p0, hipStream_t s) {
   // leaves >= 1024 workgroups; smaller problems use 4 waves (128 rows)
   FwdParams p = p0;
   const int64_t big = (int64_t)((p.Nq + 255) / 256) * p.B * p.Hq;
+  // rows are cut into 32-row segments of single block rows when block_q is
+  // not a multiple of 32 (see the kernel)
+  const bool seg = BLOCK && p.block_q % 32 != 0;
+  const int nseg = seg ? (p.Nq / p.block_q) * ((p.block_q + 31) / 32) : 0;
   if (big >= 1024) {
-    p.n_qtiles = (p.Nq + 255) / 256;
+    p.n_qtiles = seg ? (nseg + 7) / 8 : (p.Nq + 255) / 256;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BLOCK, 8>), dim3(p.n_qtiles * p.B * p.Hq),
                        dim3(512), 0, s, p);
   } else {
-    p.n_qtiles = (p.Nq + 127) / 128;
+    p.n_qtiles = seg ? (nseg + 3) / 4 : (p.Nq + 127) / 128;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BLOCK, 4>), dim3(p.n_qtiles * p.B * p.Hq),
                        dim3(256), 0, s, p);
   }

@@ -242,20 +242,24 @@ def test_causal_future_keys_are_excluded_bitwise():
     assert torch.equal(l1[:, :, :t + 1], l2[:, :, :t + 1])
 
 
+@pytest.mark.parametrize("frames,flen,blk,heads,g", [
+    (5, 128, 64, 2, 3),      # block rows a multiple of 32
+    (6, 48, 48, 4, 3),       # block rows of 48: 32 + 16-row segments
+    (16, 880, 80, 2, 7),     # the video shape, 4-wave workgroups
+    (16, 880, 80, 24, 7),    # the video shape, 8-wave workgroups
+])
 @pytest.mark.parametrize("mode", ["online", "fixed_max"])
-def test_dead_block_nan_never_read(mode):
-    """NaN in the keys/values of a key frame: queries whose frames do not
-    attend it are bit-identical to the clean run and finite. Frames of 128
-    tokens at block 64 keep every 32-row group inside one block row.
+def test_dead_block_nan_never_read(mode, frames, flen, blk, heads, g):
+    """NaN in the keys/values of key frame g: queries whose frames do not
+    attend it are bit-identical to the clean run and finite, including block
+    rows (80, 48) that are not a multiple of 32 rows.
 
     The fixed-max bound is a per-head statistic over all keys, so the frame's
     keys are scaled down in both runs: they never set max |k|, and NaN rows
     are ignored by that max, so the bound is the same in both runs."""
-    frames, flen, blk = 5, 128, 64
     n = frames * flen
     bm = frame_block_mask(frames, flen, blk)
-    q, k, v = prefill_inputs(1, 2, 2, n, n, 128, torch.bfloat16, seed=15)
-    g = 3
+    q, k, v = prefill_inputs(1, heads, heads, n, n, 128, torch.bfloat16, seed=15)
     k[:, g * flen:(g + 1) * flen] = (k[:, g * flen:(g + 1) * flen].float() * 0.25).to(torch.bfloat16)
     o1, l1 = _run(q, k, v, block_mask=bm, block=(blk, blk), softmax=mode)
     k2, v2 = k.clone(), v.clone()
@@ -265,7 +269,8 @@ def test_dead_block_nan_never_read(mode):
     for f in range(frames):
         rows = slice(f * flen, (f + 1) * flen)
         if abs(f - g) <= 1:
-            continue  # frame f attends g
+            assert torch.isnan(o2[:, rows].float()).any(), f  # frame f attends g
+            continue
         assert torch.equal(o1[:, rows], o2[:, rows]), f
         assert torch.equal(l1[:, :, rows], l2[:, :, rows]), f
         assert torch.isfinite(o2[:, rows].float()).all()
