@@ -102,6 +102,9 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
   __shared__ __attribute__((aligned(16))) __bf16 sV0[BK * D];
   __shared__ __attribute__((aligned(16))) __bf16 sV1[BK * D];
   __shared__ short sLive[BLOCK ? kMaxLiveBlocks : 1];
+  // BLOCK: per wave, bit i says whether live-list block i is live for the
+  // wave's block row (read per tile from LDS, not from the mask in HBM)
+  __shared__ uint32_t sBits[BLOCK ? NW * (kMaxLiveBlocks / 32) : 1];
   __shared__ int sCount;
 
   const int tid = threadIdx.x;
@@ -191,19 +194,26 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
   const int n_keys = BLOCK ? n_live_keys : kv_end;
   const int n_tiles = (n_keys + BK - 1) / BK;
 
-  // BLOCK: does every row of this wave see every block of the union?
+  // BLOCK: which blocks of the union the wave's block row sees (bitmap in
+  // LDS), and whether it sees all of them
   bool wave_uniform = true;
-  int my_qb = 0;
+  uint32_t* const bits = sBits + (BLOCK ? wave * (kMaxLiveBlocks / 32) : 0);
   if constexpr (BLOCK) {
-    my_qb = (row_ok ? qrow : wave_last) / p.block_q;
-    bool ok = true;
     if (q0 < p.Nq) {
-      const int wqb0 = q0 / p.block_q, wqb1 = wave_last / p.block_q;
-      for (int i = lane; i < sCount; i += 64)
-        for (int qb = wqb0; qb <= wqb1; ++qb)
-          ok &= p.block_mask[(int64_t)qb * p.nkb + sLive[i]] != 0;
+      const int my_qb = wave_last / p.block_q;  // the wave's one block row
+      for (int base = 0; base < sCount; base += 64) {
+        const int i = base + lane;
+        const bool live = i < sCount && p.block_mask[(int64_t)my_qb * p.nkb + sLive[i]] != 0;
+        const uint64_t bal = __ballot(live);
+        const int nv = min(64, sCount - base);
+        wave_uniform &= bal == (nv == 64 ? ~0ull : ((1ull << nv) - 1ull));
+        if (lane == 0) {
+          bits[base >> 5] = (uint32_t)bal;
+          if (nv > 32) bits[(base >> 5) + 1] = (uint32_t)(bal >> 32);
+        }
+      }
+      wave_lds_sync();
     }
-    wave_uniform = __ballot(!ok) == 0ull;
   }
 
   // ---- fixed-max bound for this lane's row, and the group's eligibility
@@ -326,21 +336,21 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
       }
       if (state == 1 && tile_k0 + BK > p.Nk) state = 2;
     } else {
-      if (!wave_uniform) {
-        bool any = false;
+      // 16-key groups live for the wave (the same for every lane)
+      bool any = false, all = true;
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          const int L = tile_k0 + 16 * gi;
-          bool live = false;
-          if (L < n_live_keys)  // the same for every lane: one block row per wave
-            live = p.block_mask[(int64_t)my_qb * p.nkb + sLive[L / p.block_k]] != 0;
-          grp_live[gi] = live;
-          any |= live;
+      for (int gi = 0; gi < 4; ++gi) {
+        const int L = tile_k0 + 16 * gi;
+        bool live = L < n_live_keys;
+        if (live && !wave_uniform) {
+          const int j = L / p.block_k;
+          live = (bits[j >> 5] >> (j & 31)) & 1u;
         }
-        state = __ballot(any) ? 2 : 0;
-      } else if (CAUSAL || tile_k0 + BK > n_live_keys) {
-        state = 2;
+        grp_live[gi] = live;
+        any |= live;
+        all &= live;
       }
+      state = !any ? 0 : (all && !CAUSAL) ? 1 : 2;
     }
 
     if (state != 0) {
@@ -370,8 +380,15 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
       }
 
       // ---- mask (raw scores). Lane (qc, h), register r of block kb holds
-      // key 32kb + 8(r/4) + 4h + r%4 of the tile, query qrow.
-      if (state == 2) {
+      // key 32kb + 8(r/4) + 4h + r%4 of the tile, query qrow; key group
+      // 2kb + r/8 in every lane.
+      if (BLOCK && !CAUSAL && state == 2) {
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+          if (!grp_live[gi])
+#pragma unroll
+            for (int r = 0; r < 8; ++r) s[gi >> 1][8 * (gi & 1) + r] = kNegInf;
+      } else if (state == 2) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
