@@ -238,6 +238,9 @@ def main():
                        "flops": p.flops, "bytes": p.bytes}
     out["config"] = cfg
     out["ms_parts"] = {p.name: m for p, m in zip(parts, ms_avg)}
+    # per-call spread over the timed steps (warm: inputs resident, GPU clocks up)
+    out["ms_parts_median"] = {p.name: sorted(m)[len(m) // 2] for p, m in zip(parts, ms)}
+    out["ms_parts_min"] = {p.name: min(m) for p, m in zip(parts, ms)}
     out["roofline"] = roof
     if len(parts) > 1 and parts[1].kind == "decode":
         d = parts[1]
