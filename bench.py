@@ -100,7 +100,8 @@ class Part:
             need = bd.attn_fwd_workspace_bytes(w.B, w.Hkv, w.Nk, w.d, mode)
             self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
             self.flops, self.bytes = acc.workload_work(w, block_mask=bm)
-            self.call = lambda: bd.attn_fwd(
+            # arguments marshalled once; each step is one call into the library
+            self.call, _, _ = bd.prepare_fwd(
                 q, k, v, causal=w.causal, block_mask=self.bm,
                 block=(w.block, w.block) if self.bm is not None else None,
                 softmax=self.softmax, out=self.o, lse_out=self.lse, workspace=self.ws)
@@ -112,8 +113,8 @@ class Part:
             self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
             self.seqlens_host = sl.cpu().numpy()
             self.flops, self.bytes = acc.workload_work(w, seqlens=self.seqlens_host)
-            self.call = lambda: bd.attn_decode(ins["q"], ins["k_cache"], ins["v_cache"], sl,
-                                               out=self.o, lse_out=self.lse, workspace=self.ws)
+            self.call, _, _ = bd.prepare_decode(ins["q"], ins["k_cache"], ins["v_cache"], sl,
+                                                out=self.o, lse_out=self.lse, workspace=self.ws)
 
 
 def cpu_baseline(part, budget_s):

@@ -107,11 +107,11 @@ def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def attn_fwd(q, k, v, *, causal=False, block_mask=None, block=None, scale=None,
-             softmax="online", return_lse=True, out=None, lse_out=None, workspace=None):
-    """Exact attention of q [B,Nq,Hq,d] against k, v [B,Nk,Hkv,d] (GPU tensors,
-    bf16 or fp32). block_mask: uint8 [Nq/bq, Nk/bk] (GPU tensor or array),
-    block = (bq, bk). Returns (o, lse) with lse [B,Hq,Nq] fp32 (or None)."""
+def _fwd_setup(q, k, v, causal, block_mask, block, scale, softmax, return_lse, out, lse_out,
+               workspace):
+    """Validate, allocate what the caller did not pass, and marshal the C
+    arguments of attn_fwd. Returns (args, o, lse, keep): keep holds every
+    object the arguments point into."""
     _check_gpu(q, k, v)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("q must be [B,Nq,Hq,d]; k and v [B,Nk,Hkv,d]")
@@ -141,18 +141,50 @@ def attn_fwd(q, k, v, *, causal=False, block_mask=None, block=None, scale=None,
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     st = (_Strides * 4)(_strides4(q), _strides4(k), _strides4(v), _strides4(o))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dtype_code(q),
-                            B, Hq, Hkv, Nq, Nk, d, scale, mask_kind, _ptr(bm), bq, bk, mode,
-                            st, _ptr(workspace), ws_bytes, _stream(dev))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _dtype_code(q), B, Hq, Hkv, Nq, Nk, d,
+            scale, mask_kind, _ptr(bm), bq, bk, mode, st, _ptr(workspace), ws_bytes, _stream(dev))
+    return args, o, lse, (q, k, v, o, lse, bm, workspace, st)
+
+
+def attn_fwd(q, k, v, *, causal=False, block_mask=None, block=None, scale=None,
+             softmax="online", return_lse=True, out=None, lse_out=None, workspace=None):
+    """Exact attention of q [B,Nq,Hq,d] against k, v [B,Nk,Hkv,d] (GPU tensors,
+    bf16 or fp32). block_mask: uint8 [Nq/bq, Nk/bk] (GPU tensor or array),
+    block = (bq, bk). Returns (o, lse) with lse [B,Hq,Nq] fp32 (or None)."""
+    args, o, lse, _ = _fwd_setup(q, k, v, causal, block_mask, block, scale, softmax, return_lse,
+                                 out, lse_out, workspace)
+    rc = library().attn_fwd(*args)
     if rc != 0:
         raise MiattnError(rc, "attn_fwd")
     return o, lse
 
 
-def attn_decode(q, k_cache, v_cache, seqlens, *, scale=None, kv_splits=0, return_lse=True,
-                out=None, lse_out=None, workspace=None):
-    """Decode attention: q [B,Hq,d] bf16 against caches [B,max_len,Hkv,d] bf16 with
-    seqlens int32 [B] (all GPU tensors). Returns (o [B,Hq,d], lse [B,Hq] or None)."""
+class PreparedCall:
+    """One entry point with its C arguments marshalled once: calling it
+    enqueues the same work again (same tensors, the stream current when it
+    was prepared) with a single foreign call. The tensors it was prepared
+    with must stay alive and keep their storage."""
+
+    def __init__(self, fn, args, name, keep):
+        self._fn, self._args, self._name, self._keep = fn, args, name, keep
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != 0:
+            raise MiattnError(rc, self._name)
+
+
+def prepare_fwd(q, k, v, *, causal=False, block_mask=None, block=None, scale=None,
+                softmax="online", return_lse=True, out=None, lse_out=None, workspace=None):
+    """attn_fwd as a PreparedCall: returns (call, o, lse); every call() writes
+    o (and lse) again."""
+    args, o, lse, keep = _fwd_setup(q, k, v, causal, block_mask, block, scale, softmax,
+                                    return_lse, out, lse_out, workspace)
+    return PreparedCall(library().attn_fwd, args, "attn_fwd", keep), o, lse
+
+
+def _decode_setup(q, k_cache, v_cache, seqlens, scale, kv_splits, return_lse, out, lse_out,
+                  workspace):
     _check_gpu(q, k_cache, v_cache, seqlens)
     if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
         raise ValueError("q must be [B,Hq,d]; caches [B,max_len,Hkv,d]")
@@ -172,10 +204,27 @@ def attn_decode(q, k_cache, v_cache, seqlens, *, scale=None, kv_splits=0, return
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     st = (_Strides * 2)(_strides4(k_cache), _strides4(v_cache))
-    rc = library().attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o),
-                               _ptr(lse), _dtype_code(q), B, Hq, Hkv, max_len, d, scale,
-                               kv_splits, st, _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _stream(dev))
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse),
+            _dtype_code(q), B, Hq, Hkv, max_len, d, scale, kv_splits, st, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(dev))
+    return args, o, lse, (q, k_cache, v_cache, seqlens, o, lse, workspace, st)
+
+
+def attn_decode(q, k_cache, v_cache, seqlens, *, scale=None, kv_splits=0, return_lse=True,
+                out=None, lse_out=None, workspace=None):
+    """Decode attention: q [B,Hq,d] bf16 against caches [B,max_len,Hkv,d] bf16 with
+    seqlens int32 [B] (all GPU tensors). Returns (o [B,Hq,d], lse [B,Hq] or None)."""
+    args, o, lse, _ = _decode_setup(q, k_cache, v_cache, seqlens, scale, kv_splits, return_lse,
+                                    out, lse_out, workspace)
+    rc = library().attn_decode(*args)
     if rc != 0:
         raise MiattnError(rc, "attn_decode")
     return o, lse
+
+
+def prepare_decode(q, k_cache, v_cache, seqlens, *, scale=None, kv_splits=0, return_lse=True,
+                   out=None, lse_out=None, workspace=None):
+    """attn_decode as a PreparedCall: returns (call, o, lse)."""
+    args, o, lse, keep = _decode_setup(q, k_cache, v_cache, seqlens, scale, kv_splits,
+                                       return_lse, out, lse_out, workspace)
+    return PreparedCall(library().attn_decode, args, "attn_decode", keep), o, lse
