@@ -32,10 +32,16 @@
 //    wave whose block row sees the whole union applies no mask at all.
 //  * The softmax scale is folded into the exponent argument (one FMA per
 //    score: exp2(s * scale*log2(e) - m)), and the running max is used lazily:
-//    the reference max m of a row moves only when a tile's max exceeds it by
-//    more than kRescaleThr (log2 units), so the O rescale runs on few tiles
-//    and P stays below 2^kRescaleThr. Any reference gives the same exact
-//    result; the final division by l uses the same reference.
+//    each 32-key block is exponentiated against the row's current reference
+//    m straight away, and m moves (with the O rescale) only when a lane's
+//    sum of its 16 values exceeds kBlkSumMax, so neither the block max nor
+//    its cross-lane step is on the common path and P stays <= kBlkSumMax.
+//    Any reference gives the same exact result; the final division by l
+//    uses the same reference.
+//  * Unmasked dense tiles run as three straight-line stages in a fixed
+//    instruction order: S^T of key block 0, then block 1 with block 0's
+//    exps interleaved, PV of block 0 with block 1's exps, PV of block 1 --
+//    the wave's VALU work issues while its own products occupy the pipe.
 //  * Fixed-max softmax (TPU attention guide, 4단계): the per-row bound
 //    M_i = scale*|q_i|*rho replaces the running max, removing the max
 //    reduction and the accumulator rescale; a 32-row group whose bound is too
@@ -53,7 +59,7 @@ namespace miattn {
 namespace {
 
 constexpr int BK = 64;   // keys per tile
-constexpr float kRescaleThr = 8.f;  // lazy rescale threshold, log2 units
+constexpr float kBlkSumMax = 4096.f;  // lazy rescale: a lane's 16-value block sum above this
 
 // LDS swizzles on 16-byte chunks, chosen so the MFMA-side reads hit distinct
 // banks: K is read 16 rows x one chunk per 16 lanes; V is read by the
@@ -246,7 +252,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
     }
     m_fix = p.scale * (qk + qn * rho) * kLog2e;
     const float gap = row_ok ? 2.f * p.scale * qn * rho : 0.f;
-    fixed = wave_max(gap) <= kTau;
+    fixed = __builtin_amdgcn_readfirstlane((int)(wave_max(gap) <= kTau)) != 0;
   }
 
   // ---- staging: instruction j of this wave fills tile rows
@@ -308,7 +314,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[mb][r] = 0.f;
-  float m_run = kNegInf;  // reference max (log2 units), online mode
+  float m_run = -__FLT_MAX__;  // reference max (log2 units), online mode; none yet
   float l_run = 0.f;      // this lane's partial row sum (half of the keys)
   const float c = p.scale_log2;
 
@@ -353,140 +359,283 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
       state = !any ? 0 : (all && !CAUSAL) ? 1 : 2;
     }
 
-    if (state != 0) {
-      // ---- S^T = K Q^T for two 32-key blocks
-      f32x16 s[2];
+    // ---- S^T = K Q^T for the tile's two 32-key blocks (generic path)
+    f32x16 s[2];
+    // K fragment of block kb, k-step ks: row 32kb + qc, chunk 2ks + h
+    auto kfrag = [&](int kb, int ks) {
+      const int row = 32 * kb + qc;
+      return *(const bf16x8*)(sk + row * D + kswz<D>(row, 2 * ks + h) * 8);
+    };
+    auto qk = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      // K fragment of block kb, k-step ks: row 32kb + qc, chunk 2ks + h
-      auto kfrag = [&](int kb, int ks) {
-        const int row = 32 * kb + qc;
-        return *(const bf16x8*)(sk + row * D + kswz<D>(row, 2 * ks + h) * 8);
-      };
-      bf16x8 ka = kfrag(0, 0), kc = kfrag(1, 0);
+      bf16x8 k0 = kfrag(0, 0), k1 = kfrag(0, 1);
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        bf16x8 na = ka, nc = kc;
-        if (ks + 1 < KSTEPS) {
-          na = kfrag(0, ks + 1);
-          nc = kfrag(1, ks + 1);
-        }
-        s[0] = mfma32(ka, qf[ks], s[0]);
-        s[1] = mfma32(kc, qf[ks], s[1]);
-        ka = na;
-        kc = nc;
+      for (int i = 0; i < 2 * KSTEPS; ++i) {
+        bf16x8 nx = k1;
+        if (i + 2 < 2 * KSTEPS) nx = kfrag((i + 2) / KSTEPS, (i + 2) % KSTEPS);
+        s[i / KSTEPS] = mfma32(k0, qf[i % KSTEPS], s[i / KSTEPS]);
+        k0 = k1;
+        k1 = nx;
       }
+    };
 
-      // ---- mask (raw scores). Lane (qc, h), register r of block kb holds
-      // key 32kb + 8(r/4) + 4h + r%4 of the tile, query qrow; key group
-      // 2kb + r/8 in every lane.
-      if (BLOCK && !CAUSAL && state == 2) {
+    // ---- mask of block kb (raw scores), without branches. Lane (qc, h),
+    // register r of block kb holds key 32kb + 8(r/4) + 4h + r%4 of the tile,
+    // query qrow; key group 2kb + r/8 in every lane.
+    auto mask_block = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi)
-          if (!grp_live[gi])
-#pragma unroll
-            for (int r = 0; r < 8; ++r) s[gi >> 1][8 * (gi & 1) + r] = kNegInf;
-      } else if (state == 2) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kk = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);  // key within tile
-            bool ok;
-            if constexpr (!BLOCK) {
-              const int key = tile_k0 + kk;
-              ok = key < p.Nk;
-              if (CAUSAL) ok = ok && key <= qrow + p.causal_off;
-            } else {
-              const int L = tile_k0 + kk;
-              ok = L < n_live_keys && grp_live[kk >> 4];
-              if (CAUSAL && ok) {
-                const int blk = L / p.block_k;
-                const int key = (int)sLive[blk] * p.block_k + (L - blk * p.block_k);
-                ok = key <= qrow + p.causal_off;
-              }
-            }
-            if (!ok) s[kb][r] = kNegInf;
+      for (int r = 0; r < 16; ++r) {
+        const int kk = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);  // key within tile
+        bool ok;
+        if constexpr (!BLOCK) {
+          const int key = tile_k0 + kk;
+          ok = key < p.Nk;
+          if (CAUSAL) ok = ok && key <= qrow + p.causal_off;
+        } else if constexpr (!CAUSAL) {
+          ok = grp_live[kk >> 4];  // dead tail groups are not live either
+        } else {
+          const int L = tile_k0 + kk;
+          ok = L < n_live_keys && grp_live[kk >> 4];
+          if (ok) {
+            const int blk = L / p.block_k;
+            const int key = (int)sLive[blk] * p.block_k + (L - blk * p.block_k);
+            ok = key <= qrow + p.causal_off;
           }
+        }
+        s[kb][r] = ok ? s[kb][r] : kNegInf;
       }
+    };
 
-      // ---- softmax update: p = exp2(s * c - m), one FMA + one exp per score
-      float m_use;
-      if (!fixed) {
+    auto exps = [&](const f32x16& sb, f32x16& e, float m) __attribute__((always_inline)) {
+      e[0] = ex2(__builtin_fmaf(sb[0], c, -m));
+      e[1] = ex2(__builtin_fmaf(sb[1], c, -m));
+      float l0 = e[0], l1 = e[1];
+#pragma unroll
+      for (int r = 2; r < 16; r += 2) {
+        e[r] = ex2(__builtin_fmaf(sb[r], c, -m));
+        e[r + 1] = ex2(__builtin_fmaf(sb[r + 1], c, -m));
+        l0 += e[r];
+        l1 += e[r + 1];
+      }
+      return l0 + l1;
+    };
+    // Lazy reference max: the exps of a 32-key block are taken against the
+    // row's current reference m without moving it first. Only when some
+    // lane's sum of its 16 values exceeds kBlkSumMax (a value above
+    // kBlkSumMax/16 appeared, or the row has no reference yet: m = -FLT_MAX
+    // sends every finite score to inf) does the wave take the block's exact
+    // max, move m, rescale O and l, and evaluate the block again. Any
+    // reference gives the same exact result, and P stays <= kBlkSumMax.
+    auto settle = [&](const f32x16& sb, f32x16& e, float& lb) __attribute__((always_inline)) {
+      if (!fixed && __ballot(lb > kBlkSumMax)) {
         float mx = kNegInf;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sb[r]);
+        mx = fmaxf(mx, shfl_xor(mx, 32)) * c;
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = ex2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, shfl_xor(mx, 32)) * c;  // tile max of the row, log2 units
-        if (__ballot(mx > m_run + kRescaleThr)) {
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = ex2(m_run - (m_new == kNegInf ? 0.f : m_new));
-          m_run = m_new;
-          l_run *= alpha;
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
-        }
-        m_use = m_run == kNegInf ? 0.f : m_run;
-      } else {
-        m_use = m_fix;
+          for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
+        lb = exps(sb, e, m_new);
       }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = ex2(__builtin_fmaf(s[kb][r], c, -m_use));
-          s[kb][r] = e;
-          l_run += e;
-        }
+      l_run += lb;
+    };
 
-      // ---- O^T += V^T P^T, four 16-key steps. Step u uses registers
-      // 8(u%2) .. +7 of block u/2: keys 16u + 4h + e (e < 4) and
-      // 16u + 8 + 4h + (e - 4) (e >= 4) for query c -- the B operand as is.
-      // A operand of step u, block mb (V^T rows 32mb..+31, the step's 16
-      // keys): two transpose reads, keys 16u + 8rr + 4h' + j of the groups
-      auto vfrag = [&](int u, int mb) {
-        const int ch = 4 * mb + tr_ch;
-        const int r0 = 16 * u + tr_row, r1 = 16 * u + 8 + tr_row;
-        const s16x4 lo = lds_tr16(sv + r0 * D + vswz<D>(r0, ch) * 8 + tr_half);
-        const s16x4 hi = lds_tr16(sv + r1 * D + vswz<D>(r1, ch) * 8 + tr_half);
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
+    // one 32-key block of the generic path: exps, lazy check, P in place
+    auto softmax_block = [&](int kb) __attribute__((always_inline)) {
+      f32x16 e;
+      float lb = exps(s[kb], e, fixed ? m_fix : m_run);
+      settle(s[kb], e, lb);
+      s[kb] = e;
+    };
+
+    // ---- O^T += V^T P^T, four 16-key steps. Step u uses registers
+    // 8(u%2) .. +7 of block u/2: keys 16u + 4h + e (e < 4) and
+    // 16u + 8 + 4h + (e - 4) (e >= 4) for query c -- the B operand as is.
+    // A operand of step u, block mb (V^T rows 32mb..+31, the step's 16
+    // keys): two transpose reads, keys 16u + 8rr + 4h' + j of the groups
+    auto vfrag = [&](int u, int mb) {
+      const int ch = 4 * mb + tr_ch;
+      const int r0 = 16 * u + tr_row, r1 = 16 * u + 8 + tr_row;
+      const s16x4 lo = lds_tr16(sv + r0 * D + vswz<D>(r0, ch) * 8 + tr_half);
+      const s16x4 hi = lds_tr16(sv + r1 * D + vswz<D>(r1, ch) * 8 + tr_half);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // PV of the 32-key block kb (steps 2kb, 2kb+1)
+    auto pv_block = [&](int kb) __attribute__((always_inline)) {
+      const f32x16& sb = s[kb];
       if constexpr (BLOCK) {
         // key group u is live or dead for the whole wave (one block row):
         // dead groups are skipped, so their V rows never meet the wave's P
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int uu = 0; uu < 2; ++uu) {
+          const int u = 2 * kb + uu;
           if (!grp_live[u]) continue;
-          const f32x16& sb = s[u >> 1];
-          const int o8 = 8 * (u & 1);
+          const int o8 = 8 * uu;
           const bf16x8 pf = cvt8(sb[o8 + 0], sb[o8 + 1], sb[o8 + 2], sb[o8 + 3], sb[o8 + 4],
                                  sb[o8 + 5], sb[o8 + 6], sb[o8 + 7]);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) oacc[mb] = mfma32(vfrag(u, mb), pf, oacc[mb]);
         }
-        return;
-      }
-      bf16x8 vcur = vfrag(0, 0);
+      } else {
+        bf16x8 vcur = vfrag(2 * kb, 0);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const f32x16& sb = s[u >> 1];
-        const int o8 = 8 * (u & 1);
-        const bf16x8 pf = cvt8(sb[o8 + 0], sb[o8 + 1], sb[o8 + 2], sb[o8 + 3], sb[o8 + 4],
-                               sb[o8 + 5], sb[o8 + 6], sb[o8 + 7]);
+        for (int uu = 0; uu < 2; ++uu) {
+          const int o8 = 8 * uu;
+          const bf16x8 pf = cvt8(sb[o8 + 0], sb[o8 + 1], sb[o8 + 2], sb[o8 + 3], sb[o8 + 4],
+                                 sb[o8 + 5], sb[o8 + 6], sb[o8 + 7]);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int nxt = u * MB + mb + 1;
-          bf16x8 vnext = vcur;
-          if (nxt < 4 * MB) vnext = vfrag(nxt / MB, nxt % MB);
-          oacc[mb] = mfma32(vcur, pf, oacc[mb]);
-          vcur = vnext;
+          for (int mb = 0; mb < MB; ++mb) {
+            const int nxt = uu * MB + mb + 1;
+            bf16x8 vnext = vcur;
+            if (nxt < 2 * MB) vnext = vfrag(2 * kb + nxt / MB, nxt % MB);
+            oacc[mb] = mfma32(vcur, pf, oacc[mb]);
+            vcur = vnext;
+          }
         }
       }
+    };
+    auto body = [&](auto maskc) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(maskc)::value;
+      qk();
+      if constexpr (MASK) mask_block(0);
+      softmax_block(0);
+      pv_block(0);
+      if constexpr (MASK) mask_block(1);
+      softmax_block(1);
+      pv_block(1);
+    };
+    // ---- the unmasked dense tile as three straight-line stages with a fixed
+    // instruction order (sched_barrier between steps), so the wave's own
+    // exp2 work issues while its products run in the matrix pipe:
+    //   1. S^T of key block 0, then of block 1 interleaved with block 0's exps
+    //   2. PV of block 0 interleaved with block 1's exps
+    //   3. PV of block 1
+    // with each block's (rare) rescale between the stages.
+    constexpr int NPV = 2 * MB;  // PV MFMAs per 32-key block
+    // Softmax of one 16-value block as a software pipeline over NC chunks:
+    // chunk j issues the FMAs of values 2j, 2j+1, the exp2 of 2j-2, 2j-1 and
+    // the sums of 2j-4, 2j-3 (the lags cover the exp latency).
+    struct SmPipe {
+      f32x16 x, e;
+      float l0, l1;
+    };
+    auto sm_chunk = [&](SmPipe& P, const f32x16& sb, float m, int j) __attribute__((always_inline)) {
+      if (j < 8) {
+        P.x[2 * j] = __builtin_fmaf(sb[2 * j], c, -m);
+        P.x[2 * j + 1] = __builtin_fmaf(sb[2 * j + 1], c, -m);
+      }
+      if (j >= 1 && j <= 8) {
+        P.e[2 * j - 2] = ex2(P.x[2 * j - 2]);
+        P.e[2 * j - 1] = ex2(P.x[2 * j - 1]);
+      }
+      if (j == 2) {
+        P.l0 = P.e[0];
+        P.l1 = P.e[1];
+      } else if (j >= 3 && j <= 9) {
+        P.l0 += P.e[2 * j - 4];
+        P.l1 += P.e[2 * j - 3];
+      }
+    };
+    auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+    auto body_fast = [&]() __attribute__((always_inline)) {
+      // ---- stage 1: S^T block 0, then block 1 with block 0's softmax
+      constexpr int NK = 2 * KSTEPS;   // K fragments per tile
+      constexpr int LEAD = 3;          // K fragments in flight
+      bf16x8 kf[NK];
+#pragma unroll
+      for (int i = 0; i < LEAD; ++i) kf[i] = kfrag(i / KSTEPS, i % KSTEPS);
+      fence();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      const float m0 = fixed ? m_fix : m_run;
+      SmPipe P0;
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        s[i / KSTEPS] = mfma32(kf[i], qf[i % KSTEPS], s[i / KSTEPS]);
+        if (i + LEAD < NK) kf[i + LEAD] = kfrag((i + LEAD) / KSTEPS, (i + LEAD) % KSTEPS);
+        // block 0's softmax starts one product after block 0 is complete
+        const int j0 = i - KSTEPS - 1;
+        if (j0 >= 0) {
+          if constexpr (KSTEPS == 8) {
+            sm_chunk(P0, s[0], m0, j0);
+          } else {
+            sm_chunk(P0, s[0], m0, 2 * j0);
+            sm_chunk(P0, s[0], m0, 2 * j0 + 1);
+          }
+        }
+        fence();
+      }
+      // rest of block 0's softmax, then the first V fragments of stage 2
+      {
+        constexpr int done = KSTEPS == 8 ? KSTEPS - 1 : 2 * (KSTEPS - 1);
+#pragma unroll
+        for (int j = done; j < 10; ++j) sm_chunk(P0, s[0], m0, j);
+      }
+      constexpr int VLEAD = 3;  // V fragments in flight
+      bf16x8 vf[NPV];
+#pragma unroll
+      for (int j = 0; j < VLEAD; ++j) vf[j] = vfrag(j / MB, j % MB);
+      float lb0 = P0.l0 + P0.l1;
+      f32x16 e0 = P0.e;
+      fence();
+      settle(s[0], e0, lb0);
+      // ---- stage 2: PV of block 0 with block 1's softmax
+      const float m1 = fixed ? m_fix : m_run;
+      SmPipe P1;
+      bf16x8 pf[2];
+      pf[0] = cvt8(e0[0], e0[1], e0[2], e0[3], e0[4], e0[5], e0[6], e0[7]);
+      fence();
+#pragma unroll
+      for (int j = 0; j < NPV; ++j) {
+        if (j == 1) pf[1] = cvt8(e0[8], e0[9], e0[10], e0[11], e0[12], e0[13], e0[14], e0[15]);
+        oacc[j % MB] = mfma32(vf[j], pf[j / MB], oacc[j % MB]);
+        if (j + VLEAD < NPV) vf[j + VLEAD] = vfrag((j + VLEAD) / MB, (j + VLEAD) % MB);
+        if constexpr (NPV == 8) {
+          sm_chunk(P1, s[1], m1, j);
+        } else {
+          sm_chunk(P1, s[1], m1, 2 * j);
+          sm_chunk(P1, s[1], m1, 2 * j + 1);
+        }
+        fence();
+      }
+      {
+        constexpr int done = NPV == 8 ? NPV : 2 * NPV;
+#pragma unroll
+        for (int j = done; j < 10; ++j) sm_chunk(P1, s[1], m1, j);
+      }
+#pragma unroll
+      for (int j = 0; j < VLEAD; ++j) vf[j] = vfrag(2 + j / MB, j % MB);
+      float lb1 = P1.l0 + P1.l1;
+      f32x16 e1 = P1.e;
+      fence();
+      settle(s[1], e1, lb1);
+      // ---- stage 3: PV of block 1
+      pf[0] = cvt8(e1[0], e1[1], e1[2], e1[3], e1[4], e1[5], e1[6], e1[7]);
+      fence();
+#pragma unroll
+      for (int j = 0; j < NPV; ++j) {
+        if (j == 1) pf[1] = cvt8(e1[8], e1[9], e1[10], e1[11], e1[12], e1[13], e1[14], e1[15]);
+        oacc[j % MB] = mfma32(vf[j], pf[j / MB], oacc[j % MB]);
+        if (j + VLEAD < NPV) vf[j + VLEAD] = vfrag(2 + (j + VLEAD) / MB, (j + VLEAD) % MB);
+        fence();
+      }
+    };
+    if constexpr (!BLOCK) {
+      if (state == 1) body_fast();
+      else if (state == 2) body(std::true_type());
+    } else {
+      if (state == 1) body(std::false_type());
+      else if (state == 2) body(std::true_type());
     }
   };
 
