@@ -630,13 +630,9 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
         fence();
       }
     };
-    if constexpr (!BLOCK) {
-      if (state == 1) body_fast();
-      else if (state == 2) body(std::true_type());
-    } else {
-      if (state == 1) body(std::false_type());
-      else if (state == 2) body(std::true_type());
-    }
+    // state 1 has every key group live (and no causal rule), dense or block
+    if (state == 1) body_fast();
+    else if (state == 2) body(std::true_type());
   };
 
   if (n_tiles > 0) issue_tile(0, std::integral_constant<int, 0>());
