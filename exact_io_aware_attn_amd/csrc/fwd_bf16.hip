@@ -93,20 +93,29 @@ __device__ __forceinline__ void map_workgroup(int i, int G, int nX, int& X, int&
   }
 }
 
-// NW waves per workgroup (4 or 8), 32 query rows per wave
-template <int D, bool CAUSAL, bool BLOCK, int NW>
+// NW waves per workgroup (4 or 8), 32 query rows per wave. KS = 2 splits
+// the keys of each 32-row block between two waves (alternate tiles), whose
+// partial (m, l, O) are merged at the end: half the serial tile chain per
+// row, for problems too small to fill the chip with whole rows.
+//
+// FX: fixed-max mode compiled in. There O is divided by the sum of the bf16
+// weights it was accumulated with (exact for a single visible key, where the
+// bound leaves P well below 1 and its rounding would otherwise show), and
+// the LSE uses the fp32 sum.
+template <int D, bool CAUSAL, bool BLOCK, int NW, int KS = 1, bool FX = false>
 __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdParams p) {
-  constexpr int BQ = 32 * NW;        // query rows per workgroup
+  static_assert(KS == 1 || !BLOCK, "key split: dense masks only");
+  constexpr int RW = NW / KS;        // waves per key share (one per 32-row block)
+  constexpr int BQ = 32 * RW;        // query rows per workgroup
   constexpr int CH = D / 8;          // 16-byte chunks per K/V row
   constexpr int KSTEPS = D / 16;     // k-steps of the S^T MFMA
   constexpr int MB = D / 32;         // 32-row blocks of O^T
   constexpr int RPI = 1024 / (D * 2);  // tile rows per 1 KiB load instruction
   constexpr int NIW = BK / RPI / NW;   // load instructions per wave per tile
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK0[BK * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sK1[BK * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sV0[BK * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sV1[BK * D];
+  // K/V tiles: buffer BUF of key share k is [BUF * KS + k]
+  __shared__ __attribute__((aligned(16))) __bf16 sKb[2 * KS][BK * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sVb[2 * KS][BK * D];
   __shared__ short sLive[BLOCK ? kMaxLiveBlocks : 1];
   // BLOCK: per wave, bit i says whether live-list block i is live for the
   // wave's block row (read per tile from LDS, not from the mask in HBM)
@@ -118,6 +127,8 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
   const int wave = tid >> 6;
   const int qc = lane & 31;  // query column of this lane
   const int h = lane >> 5;  // which half of each 8-row group of keys
+  const int rw = wave % RW;  // 32-row block of this wave
+  const int kp = wave / RW;  // key share of this wave (tiles t with t % KS == kp)
 
   const int G = p.Hq / p.Hkv;
   int X, g;
@@ -148,7 +159,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
   } else {
     q_start = qt * BQ;
     q_end = min(q_start + BQ, p.Nq);
-    q0 = q_start + wave * 32;
+    q0 = q_start + rw * 32;
     nrows = 32;
   }
   const int qrow = q0 + qc;
@@ -274,22 +285,30 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
   // BLOCK: one resource over all Nk rows, rows gathered by key index
   const rsrc_t rk_all = make_rsrc(kg, span(p.Nk, p.k_ss));
   const rsrc_t rv_all = make_rsrc(vg, span(p.Nk, p.v_ss));
-  auto issue_tile = [&](int t, auto bufc) {
+  // step st loads tiles st * KS + k, k < KS (tiles past the end read as
+  // zeros: their range is empty)
+  auto issue_tile = [&](int st, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
-    __bf16* const dk = BUF ? sK1 : sK0;
-    __bf16* const dv = BUF ? sV1 : sV0;
     if constexpr (!BLOCK) {
-      const int r0 = t * BK;
-      const int nvalid = min(BK, kv_end - r0);
-      const rsrc_t rk = make_rsrc(kg + (int64_t)r0 * p.k_ss, span(nvalid, p.k_ss));
-      const rsrc_t rv = make_rsrc(vg + (int64_t)r0 * p.v_ss, span(nvalid, p.v_ss));
 #pragma unroll
-      for (int j = 0; j < NIW; ++j) {
-        const int lds_row = (wave * NIW + j) * RPI;
-        buf_load_lds16(rk, dk + lds_row * D, dko[j]);
-        buf_load_lds16(rv, dv + lds_row * D, dvo[j]);
+      for (int k = 0; k < KS; ++k) {
+        __bf16* const dk = sKb[BUF * KS + k];
+        __bf16* const dv = sVb[BUF * KS + k];
+        const int r0 = (st * KS + k) * BK;
+        const int nvalid = min(BK, kv_end - r0);
+        const rsrc_t rk = make_rsrc(kg + (int64_t)r0 * p.k_ss, span(nvalid, p.k_ss));
+        const rsrc_t rv = make_rsrc(vg + (int64_t)r0 * p.v_ss, span(nvalid, p.v_ss));
+#pragma unroll
+        for (int j = 0; j < NIW; ++j) {
+          const int lds_row = (wave * NIW + j) * RPI;
+          buf_load_lds16(rk, dk + lds_row * D, dko[j]);
+          buf_load_lds16(rv, dv + lds_row * D, dvo[j]);
+        }
       }
     } else {
+      const int t = st;
+      __bf16* const dk = sKb[BUF];
+      __bf16* const dv = sVb[BUF];
 #pragma unroll
       for (int j = 0; j < NIW; ++j) {
         const int r = dma_row0 + j * RPI;
@@ -316,6 +335,17 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
     for (int r = 0; r < 16; ++r) oacc[mb][r] = 0.f;
   float m_run = -__FLT_MAX__;  // reference max (log2 units), online mode; none yet
   float l_run = 0.f;      // this lane's partial row sum (half of the keys)
+  float l_rnd = 0.f;      // FX: the same sum over the bf16-rounded weights
+  // FX: add the eight bf16 weights of a PV operand to l_rnd
+  auto sum_rounded = [&](const bf16x8& pf) __attribute__((always_inline)) {
+    if constexpr (FX) {
+      const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+      l_rnd = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), one2, l_rnd, false);
+      l_rnd = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), one2, l_rnd, false);
+      l_rnd = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), one2, l_rnd, false);
+      l_rnd = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), one2, l_rnd, false);
+    }
+  };
   const float c = p.scale_log2;
 
   // per-lane address pieces for the V^T transpose reads (see PV below)
@@ -324,16 +354,17 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
   const int tr_half = 4 * (lane & 1);
 
   // one tile of keys from LDS buffer BUF (compile-time)
-  auto tile_body = [&](int t, auto bufc) {
+  auto tile_body = [&](int st, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
-    const __bf16* const sk = BUF ? sK1 : sK0;
-    const __bf16* const sv = BUF ? sV1 : sV0;
+    const int t = st * KS + kp;
+    const __bf16* const sk = sKb[BUF * KS + kp];
+    const __bf16* const sv = sVb[BUF * KS + kp];
     // ---- what this wave has to do with this tile
     // state 0: nothing visible, 1: everything visible, 2: apply the mask
     int state = 1;
     bool grp_live[4] = {true, true, true, true};  // BLOCK, per 16-key group
     const int tile_k0 = t * BK;
-    if (q0 >= p.Nq) {
+    if (q0 >= p.Nq || tile_k0 >= n_keys) {
       state = 0;
     } else if constexpr (!BLOCK) {
       if (CAUSAL) {
@@ -439,6 +470,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
         const float alpha = ex2(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
+        l_rnd *= alpha;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -481,6 +513,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
           const int o8 = 8 * uu;
           const bf16x8 pf = cvt8(sb[o8 + 0], sb[o8 + 1], sb[o8 + 2], sb[o8 + 3], sb[o8 + 4],
                                  sb[o8 + 5], sb[o8 + 6], sb[o8 + 7]);
+          sum_rounded(pf);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) oacc[mb] = mfma32(vfrag(u, mb), pf, oacc[mb]);
         }
@@ -491,6 +524,7 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
           const int o8 = 8 * uu;
           const bf16x8 pf = cvt8(sb[o8 + 0], sb[o8 + 1], sb[o8 + 2], sb[o8 + 3], sb[o8 + 4],
                                  sb[o8 + 5], sb[o8 + 6], sb[o8 + 7]);
+          sum_rounded(pf);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
             const int nxt = uu * MB + mb + 1;
@@ -594,10 +628,14 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
       SmPipe P1;
       bf16x8 pf[2];
       pf[0] = cvt8(e0[0], e0[1], e0[2], e0[3], e0[4], e0[5], e0[6], e0[7]);
+      sum_rounded(pf[0]);
       fence();
 #pragma unroll
       for (int j = 0; j < NPV; ++j) {
-        if (j == 1) pf[1] = cvt8(e0[8], e0[9], e0[10], e0[11], e0[12], e0[13], e0[14], e0[15]);
+        if (j == 1) {
+          pf[1] = cvt8(e0[8], e0[9], e0[10], e0[11], e0[12], e0[13], e0[14], e0[15]);
+          sum_rounded(pf[1]);
+        }
         oacc[j % MB] = mfma32(vf[j], pf[j / MB], oacc[j % MB]);
         if (j + VLEAD < NPV) vf[j + VLEAD] = vfrag((j + VLEAD) / MB, (j + VLEAD) % MB);
         if constexpr (NPV == 8) {
@@ -621,10 +659,14 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
       settle(s[1], e1, lb1);
       // ---- stage 3: PV of block 1
       pf[0] = cvt8(e1[0], e1[1], e1[2], e1[3], e1[4], e1[5], e1[6], e1[7]);
+      sum_rounded(pf[0]);
       fence();
 #pragma unroll
       for (int j = 0; j < NPV; ++j) {
-        if (j == 1) pf[1] = cvt8(e1[8], e1[9], e1[10], e1[11], e1[12], e1[13], e1[14], e1[15]);
+        if (j == 1) {
+          pf[1] = cvt8(e1[8], e1[9], e1[10], e1[11], e1[12], e1[13], e1[14], e1[15]);
+          sum_rounded(pf[1]);
+        }
         oacc[j % MB] = mfma32(vf[j], pf[j / MB], oacc[j % MB]);
         if (j + VLEAD < NPV) vf[j + VLEAD] = vfrag(2 + (j + VLEAD) / MB, (j + VLEAD) % MB);
         fence();
@@ -635,23 +677,61 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
     else if (state == 2) body(std::true_type());
   };
 
-  if (n_tiles > 0) issue_tile(0, std::integral_constant<int, 0>());
+  const int n_steps = (n_tiles + KS - 1) / KS;
+  if (n_steps > 0) issue_tile(0, std::integral_constant<int, 0>());
   __syncthreads();
-  for (int t = 0; t < n_tiles; t += 2) {
-    if (t + 1 < n_tiles) issue_tile(t + 1, std::integral_constant<int, 1>());
-    tile_body(t, std::integral_constant<int, 0>());
-    __syncthreads();  // buffer 0 free; tile t+1 landed in buffer 1
-    if (t + 1 < n_tiles) {
-      if (t + 2 < n_tiles) issue_tile(t + 2, std::integral_constant<int, 0>());
-      tile_body(t + 1, std::integral_constant<int, 1>());
+  for (int st = 0; st < n_steps; st += 2) {
+    if (st + 1 < n_steps) issue_tile(st + 1, std::integral_constant<int, 1>());
+    tile_body(st, std::integral_constant<int, 0>());
+    __syncthreads();  // buffer set 0 free; step st+1 landed in set 1
+    if (st + 1 < n_steps) {
+      if (st + 2 < n_steps) issue_tile(st + 2, std::integral_constant<int, 0>());
+      tile_body(st + 1, std::integral_constant<int, 1>());
       __syncthreads();
     }
+  }
+
+  float m_ref = fixed ? m_fix : m_run;
+  if constexpr (KS > 1) {
+    // ---- merge the key shares of each row block: wave rw + RW hands its
+    // (m, l, O) to wave rw through LDS (the K/V buffers are free now); the
+    // pages' block-merge rule, O = sum_s 2^(m_s - m) O_s, l likewise
+    static_assert(KS == 2, "two key shares");
+    constexpr int NX = MB * 16 + 3;  // floats per lane handed over
+    static_assert(RW * NX * 64 * 4 <= (int)sizeof(sKb), "merge area");
+    float* const xch = reinterpret_cast<float*>(&sKb[0][0]) + rw * NX * 64 + lane;
+    if (kp == 1) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[(mb * 16 + r) * 64] = oacc[mb][r];
+      xch[(MB * 16) * 64] = m_ref;
+      xch[(MB * 16 + 1) * 64] = l_run;
+      xch[(MB * 16 + 2) * 64] = l_rnd;
+    }
+    __syncthreads();
+    if (kp != 0) return;
+    const float m1 = xch[(MB * 16) * 64];
+    const float l1 = xch[(MB * 16 + 1) * 64];
+    const float m = fmaxf(m_ref, m1);
+    const float a0 = ex2(m_ref - m), a1 = ex2(m1 - m);
+    l_run = l_run * a0 + l1 * a1;
+    l_rnd = l_rnd * a0 + xch[(MB * 16 + 2) * 64] * a1;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[mb][r] = oacc[mb][r] * a0 + xch[(mb * 16 + r) * 64] * a1;
+    m_ref = m;
   }
 
   // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2
   const float l_tot = l_run + shfl_xor(l_run, 32);
   const bool live = l_tot > 0.f;
-  const float inv = live ? 1.f / l_tot : 0.f;
+  float inv = live ? 1.f / l_tot : 0.f;
+  if constexpr (FX) {
+    const float r_tot = l_rnd + shfl_xor(l_rnd, 32);
+    inv = live && r_tot > 0.f ? 1.f / r_tot : 0.f;
+  }
   if (row_ok) {
     __bf16* op = (__bf16*)p.o + b * p.o_sb + (int64_t)qrow * p.o_ss + hq * p.o_sh;
 #pragma unroll
@@ -662,14 +742,22 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdPara
                                oacc[mb][4 * jj + 2] * inv, oacc[mb][4 * jj + 3] * inv);
         *(bf16x4*)(op + 32 * mb + 8 * jj + 4 * h) = v4;
       }
-    if (p.lse != nullptr && h == 0) {
-      const float m_ref = fixed ? m_fix : m_run;
+    if (p.lse != nullptr && h == 0)
       p.lse[((int64_t)b * p.Hq + hq) * p.Nq + qrow] = live ? (m_ref + log2f(l_tot)) * kLn2 : kNegInf;
-    }
   }
 }
 
-template <int D, bool CAUSAL, bool BLOCK>
+// the key split is used for d = 64 dense problems with at least four key
+// tiles whose 128-row workgroups would be fewer than two per CU (512): there
+// the serial tile chain of the longest rows sets the time; with more
+// workgroups the doubled K/V staging per row costs more than it saves
+template <int D, bool BLOCK>
+bool key_split(const FwdParams& p) {
+  const int64_t wg128 = (int64_t)((p.Nq + 127) / 128) * p.B * p.Hq;
+  return !BLOCK && D == 64 && (p.Nk + BK - 1) / BK >= 4 && wg128 < 512;
+}
+
+template <int D, bool CAUSAL, bool BLOCK, bool FX>
 hipError_t launch_one(const FwdParams& p0, hipStream_t s) {
   // 8 waves (256 rows) per workgroup share each K/V tile when that still
   // leaves >= 1024 workgroups; smaller problems use 4 waves (128 rows)
@@ -681,14 +769,25 @@ hipError_t launch_one(const FwdParams& p0, hipStream_t s) {
   const int nseg = seg ? (p.Nq / p.block_q) * ((p.block_q + 31) / 32) : 0;
   if (big >= 1024) {
     p.n_qtiles = seg ? (nseg + 7) / 8 : (p.Nq + 255) / 256;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BLOCK, 8>), dim3(p.n_qtiles * p.B * p.Hq),
-                       dim3(512), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BLOCK, 8, 1, FX>),
+                       dim3(p.n_qtiles * p.B * p.Hq), dim3(512), 0, s, p);
+  } else if (key_split<D, BLOCK>(p)) {
+    // few workgroups of whole rows: 64 rows per workgroup, keys split in two
+    p.n_qtiles = (p.Nq + 63) / 64;
+    if constexpr (!BLOCK && D == 64)
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, 4, 2, FX>),
+                         dim3(p.n_qtiles * p.B * p.Hq), dim3(256), 0, s, p);
   } else {
     p.n_qtiles = seg ? (nseg + 3) / 4 : (p.Nq + 127) / 128;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BLOCK, 4>), dim3(p.n_qtiles * p.B * p.Hq),
-                       dim3(256), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BLOCK, 4, 1, FX>),
+                       dim3(p.n_qtiles * p.B * p.Hq), dim3(256), 0, s, p);
   }
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool BLOCK>
+hipError_t launch_mode(const FwdParams& p, hipStream_t s) {
+  return p.fixed ? launch_one<D, CAUSAL, BLOCK, true>(p, s) : launch_one<D, CAUSAL, BLOCK, false>(p, s);
 }
 
 }  // namespace
@@ -696,10 +795,10 @@ hipError_t launch_one(const FwdParams& p0, hipStream_t s) {
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool block, hipStream_t s) {
   if (p.Nq == 0 || p.B == 0) return hipSuccess;
 #define MIATTN_DISPATCH(DD)                                                     \
-  if (causal && block) return launch_one<DD, true, true>(p, s);                \
-  if (causal) return launch_one<DD, true, false>(p, s);                        \
-  if (block) return launch_one<DD, false, true>(p, s);                         \
-  return launch_one<DD, false, false>(p, s);
+  if (causal && block) return launch_mode<DD, true, true>(p, s);               \
+  if (causal) return launch_mode<DD, true, false>(p, s);                       \
+  if (block) return launch_mode<DD, false, true>(p, s);                        \
+  return launch_mode<DD, false, false>(p, s);
   if (d == 64) { MIATTN_DISPATCH(64) }
   MIATTN_DISPATCH(128)
 #undef MIATTN_DISPATCH

@@ -77,6 +77,22 @@ def test_bf16_eight_wave_workgroups_ragged(d, causal):
 
 
 @pytest.mark.parametrize("mode", ["online", "fixed_max"])
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,causal", [
+    (1, 4, 2, 333, 700, True),     # odd number of key tiles (11): shares of 6 and 5
+    (2, 3, 1, 257, 1000, False),   # MQA, ragged key tail
+    (1, 2, 2, 700, 333, True),     # Nq > Nk: the first 367 rows see no key
+    (1, 8, 8, 1500, 1500, True),   # long rows, several 64-row workgroups per head
+])
+def test_bf16_key_split(B, Hq, Hkv, Nq, Nk, causal, mode):
+    """d = 64 problems with few workgroups split each row's keys between two
+    waves and merge their (m, l, O): every row against the oracle."""
+    q, k, v = prefill_inputs(B, Hq, Hkv, Nq, Nk, 64, torch.bfloat16, seed=Nq + Nk + Hq)
+    o, lse = _run(q, k, v, causal=causal, softmax=mode)
+    O, L = _ref(q, k, v, 1 / 8.0, causal=causal)
+    check(o, O, lse, L, where=f"key split {mode} B={B} H={Hq}/{Hkv} N={Nq}x{Nk} causal={causal}")
+
+
+@pytest.mark.parametrize("mode", ["online", "fixed_max"])
 def test_bf16_eight_wave_frame_mask(mode):
     frames, flen, blk = 5, 128, 64
     n = frames * flen
