@@ -103,7 +103,10 @@ __device__ __forceinline__ void map_workgroup(int i, int G, int nX, int& X, int&
 // bound leaves P well below 1 and its rounding would otherwise show), and
 // the LSE uses the fp32 sum.
 template <int D, bool CAUSAL, bool BLOCK, int NW, int KS = 1, bool FX = false>
-__global__ void __launch_bounds__(64 * NW, 8 / NW) fwd_bf16_kernel(const FwdParams p) {
+// d = 64 with 4 waves and whole rows fits three workgroups per CU (<= 170
+// VGPRs, 32 KiB of LDS each)
+__global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3 : 8 / NW)
+    fwd_bf16_kernel(const FwdParams p) {
   static_assert(KS == 1 || !BLOCK, "key split: dense masks only");
   constexpr int RW = NW / KS;        // waves per key share (one per 32-row block)
   constexpr int BQ = 32 * RW;        // query rows per workgroup
