@@ -198,10 +198,23 @@ def test_empty_rows_from_block_mask():
     assert (o[:, 32:48].float() == 0).all()
 
 
-def test_single_key_returns_value_row_exactly():
+@pytest.mark.parametrize("mode", ["online", "fixed_max", "fixed_max_centered"])
+def test_single_key_returns_value_row_exactly(mode):
     q, k, v = prefill_inputs(1, 2, 1, 50, 1, 128, torch.bfloat16, seed=3)
-    o, _ = _run(q, k, v)
+    o, _ = _run(q, k, v, softmax=mode)
     assert torch.equal(o.cpu(), v.expand(1, 50, 2, 128).contiguous())
+
+
+@pytest.mark.parametrize("mode", ["online", "fixed_max"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,N", [(1, 4, 300), (32, 16, 300), (1, 8, 1500)])
+def test_first_causal_row_returns_first_value_row_exactly(mode, d, B, H, N):
+    """Row 0 of a causal problem sees key 0 only, so O[0] = V[0] exactly in
+    every kernel configuration (4- and 8-wave workgroups, key split) and in
+    the fixed-max mode too, where the weight is a rounded value below 1."""
+    q, k, v = prefill_inputs(B, H, H, N, N, d, torch.bfloat16, seed=N + d + B)
+    o, lse = _run(q, k, v, causal=True, softmax=mode)
+    assert torch.equal(o[:, 0].cpu(), v[:, 0])
 
 
 def test_identical_keys_return_mean_value():
