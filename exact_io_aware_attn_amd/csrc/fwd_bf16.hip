@@ -11,10 +11,15 @@
 //    query head) (8 when the problem still yields >= 1024 workgroups); the
 //    Q tile stays in VGPRs, O accumulates in VGPRs; K/V tiles of 64 keys go
 //    HBM -> LDS directly (buffer loads into LDS, no staging registers),
-//    double-buffered in four separate LDS arrays so the next tile's loads
-//    are in flight while the current tile is consumed. Each load
-//    instruction fills 1 KiB of LDS in lane order, so every lane fetches the
-//    global 16-byte chunk that belongs in its (swizzled) LDS slot.
+//    double-buffered so the next tile's loads are in flight while the
+//    current tile is consumed. Each load instruction fills 1 KiB of LDS in
+//    lane order, so every lane fetches the global 16-byte chunk that belongs
+//    in its (swizzled) LDS slot.
+//  * Small d = 64 problems (fewer than 512 workgroups of 128 rows) take 64
+//    rows per 4-wave workgroup and split each row block's keys between two
+//    waves (alternate tiles), merging their (m, l, O) at the end with the
+//    block-merge rule of the same pages (§2): half the serial tile chain of
+//    the longest rows, which is what sets the time there.
 //  * Each wave owns 32 query rows and computes S^T = K Q^T with
 //    v_mfma_f32_32x32x16_bf16, so every lane holds the scores of ONE query
 //    for 16 keys of a 32-key block: the row max needs one cross-lane step
@@ -45,7 +50,9 @@
 //  * Fixed-max softmax (TPU attention guide, 4단계): the per-row bound
 //    M_i = scale*|q_i|*rho replaces the running max, removing the max
 //    reduction and the accumulator rescale; a 32-row group whose bound is too
-//    loose falls back to the running max.
+//    loose falls back to the running max. O is divided by the sum of the
+//    bf16 weights that went into PV (the bound leaves every weight below 1
+//    and rounded), the LSE by the fp32 sum.
 //  * Workgroup order: heaviest causal tiles first; the query heads sharing a
 //    KV head land on the same XCD (blockIdx % 8) so K/V are reused in its L2.
 
