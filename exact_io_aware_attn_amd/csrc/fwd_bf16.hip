@@ -589,7 +589,11 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3 :
       }
     };
     auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+    // The wave's issue priority falls as it moves through the tile (2, 1, 0
+    // by stage): of the two waves sharing a SIMD, the one further behind is
+    // served first, so they reach the tile's barrier closer together.
     auto body_fast = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_s_setprio(2);
       // ---- stage 1: S^T block 0, then block 1 with block 0's softmax
       constexpr int NK = 2 * KSTEPS;   // K fragments per tile
       constexpr int LEAD = 3;          // K fragments in flight
@@ -632,6 +636,7 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3 :
       float lb0 = P0.l0 + P0.l1;
       f32x16 e0 = P0.e;
       fence();
+      __builtin_amdgcn_s_setprio(1);
       settle(s[0], e0, lb0);
       // ---- stage 2: PV of block 0 with block 1's softmax
       const float m1 = fixed ? m_fix : m_run;
@@ -666,6 +671,7 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3 :
       float lb1 = P1.l0 + P1.l1;
       f32x16 e1 = P1.e;
       fence();
+      __builtin_amdgcn_s_setprio(0);
       settle(s[1], e1, lb1);
       // ---- stage 3: PV of block 1
       pf[0] = cvt8(e1[0], e1[1], e1[2], e1[3], e1[4], e1[5], e1[6], e1[7]);
