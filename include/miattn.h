@@ -43,7 +43,7 @@ enum {
   MIATTN_OK = 0,
   MIATTN_ERR_NULL = 1,        /* a required pointer is NULL                  */
   MIATTN_ERR_SHAPE = 2,       /* sizes inconsistent or out of range          */
-  MIATTN_ERR_UNSUPPORTED = 3, /* valid request this build does not implement */
+  MIATTN_ERR_UNSUPPORTED = 3, /* valid request the library does not implement */
   MIATTN_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required  */
   MIATTN_ERR_HIP = 5,         /* a HIP runtime call or launch failed         */
   MIATTN_ERR_ARG = 6          /* a scalar argument is invalid (scale, mode)  */
