@@ -55,6 +55,11 @@ WORKLOADS = {
     "gqa-decode-b64": Workload("gqa-decode-b64", "decode", B=64, Hq=32, Hkv=8, Nq=1,
                                Nk=32768, d=128, dtype="bf16", seed=4,
                                len_lo=1024, len_hi=32768),
+    # GPT-2 medium attention (batch 64, 16 heads, length 1024, head dim 64): the shape
+    # "플래시어텐션: 메모리를 아끼는 정확한 어텐션" reports its measurement on (§4 재계산)
+    "gpt2-medium-causal": Workload("gpt2-medium-causal", "prefill", B=64, Hq=16, Hkv=16,
+                                   Nq=1024, Nk=1024, d=64, dtype="bf16", causal=True,
+                                   seed=6),
     "video-frames-16x880": Workload("video-frames-16x880", "prefill", B=1, Hq=24,
                                     Hkv=24, Nq=14080, Nk=14080, d=128, dtype="bf16",
                                     seed=5, frames=16, frame_len=880, block=80,

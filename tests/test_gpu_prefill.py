@@ -333,6 +333,10 @@ def test_full_gpt2_causal():
     _full("gpt2-causal", heads=[0, 5, 11])
 
 
+def test_full_gpt2_medium_causal():
+    _full("gpt2-medium-causal", heads=[0, 9, 15])
+
+
 def test_full_llama3_8b_gqa_causal():
     _full("llama3-8b-gqa-causal-8k", heads=[0, 3, 4, 17, 31])
 

@@ -50,5 +50,6 @@ def test_frame_mask_structure():
 
 def test_named_workloads():
     assert set(WORKLOADS) == {"tiny-f32", "gpt2-causal", "llama3-8b-gqa-causal-8k",
-                              "gqa-decode-b64", "video-frames-16x880"}
+                              "gqa-decode-b64", "video-frames-16x880",
+                              "gpt2-medium-causal"}
     assert WORKLOADS["llama3-8b-gqa-causal-8k"].scale == 1 / 128 ** 0.5
