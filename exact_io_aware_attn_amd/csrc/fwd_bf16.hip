@@ -110,9 +110,13 @@ __device__ __forceinline__ void map_workgroup(int i, int G, int nX, int& X, int&
 // bound leaves P well below 1 and its rounding would otherwise show), and
 // the LSE uses the fp32 sum.
 template <int D, bool CAUSAL, bool BLOCK, int NW, int KS = 1, bool FX = false>
-// d = 64 with 4 waves and whole rows fits three workgroups per CU (<= 170
-// VGPRs, 32 KiB of LDS each)
-__global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3 : 8 / NW)
+// waves per SIMD asked of the register allocator. d = 64 with 4 waves and
+// whole rows: three (<= 170 VGPRs, 32 KiB of LDS per workgroup, three
+// workgroups per CU). d = 64 dense with 8 waves: four (128 VGPRs, two
+// workgroups per CU; a few registers spill, off the tile loop). d = 128: two.
+__global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
+                                           : (D == 64 && NW == 8 && !BLOCK) ? 4
+                                                                            : 8 / NW)
     fwd_bf16_kernel(const FwdParams p) {
   static_assert(KS == 1 || !BLOCK, "key split: dense masks only");
   constexpr int RW = NW / KS;        // waves per key share (one per 32-row block)
@@ -776,14 +780,19 @@ bool key_split(const FwdParams& p) {
 template <int D, bool CAUSAL, bool BLOCK, bool FX>
 hipError_t launch_one(const FwdParams& p0, hipStream_t s) {
   // 8 waves (256 rows) per workgroup share each K/V tile when that still
-  // leaves >= 1024 workgroups; smaller problems use 4 waves (128 rows)
+  // leaves >= 1024 workgroups; smaller problems use 4 waves (128 rows). Dense
+  // causal d = 64 always uses 4 waves: on the diagonal of a 256-row workgroup
+  // the waves of its first rows sit idle for up to three of the tiles the
+  // last rows need, which at d = 64 (three 4-wave workgroups per CU) costs
+  // more than sharing each K/V tile among 8 waves saves
   FwdParams p = p0;
   const int64_t big = (int64_t)((p.Nq + 255) / 256) * p.B * p.Hq;
+  const bool wide = big >= 1024 && !(D == 64 && CAUSAL && !BLOCK);
   // rows are cut into 32-row segments of single block rows when block_q is
   // not a multiple of 32 (see the kernel)
   const bool seg = BLOCK && p.block_q % 32 != 0;
   const int nseg = seg ? (p.Nq / p.block_q) * ((p.block_q + 31) / 32) : 0;
-  if (big >= 1024) {
+  if (wide) {
     p.n_qtiles = seg ? (nseg + 7) / 8 : (p.Nq + 255) / 256;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BLOCK, 8, 1, FX>),
                        dim3(p.n_qtiles * p.B * p.Hq), dim3(512), 0, s, p);

@@ -63,17 +63,20 @@ def test_bf16_shapes(d, causal, Hq, Hkv, Nq, Nk):
     check(o, O, lse, L, where=f"bf16 d={d} causal={causal} H={Hq}/{Hkv} N={Nq}x{Nk}")
 
 
+@pytest.mark.parametrize("mode", ["online", "fixed_max"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bf16_eight_wave_workgroups_ragged(d, causal):
+def test_bf16_eight_wave_workgroups_ragged(d, causal, mode):
     """Enough (batch, head) pairs that the 256-row, 8-wave workgroups are used
-    (>= 1024 of them), with ragged query and key tails and GQA."""
+    (>= 1024 of them), with ragged query and key tails and GQA. Dense causal
+    d = 64 takes 4-wave workgroups at every size, so that case runs the
+    4-wave kernel with many workgroups in flight."""
     B, Hq, Hkv, Nq, Nk = 32, 16, 4, 300, 333
     q, k, v = prefill_inputs(B, Hq, Hkv, Nq, Nk, d, torch.bfloat16, seed=d + causal)
-    o, lse = _run(q, k, v, causal=causal)
+    o, lse = _run(q, k, v, causal=causal, softmax=mode)
     heads = [0, 7, 15]
     O, L = _ref(q, k, v, 1 / math.sqrt(d), causal=causal, heads=heads)
-    check(o[:, :, heads], O, lse[:, heads], L, where=f"8-wave d={d} causal={causal}")
+    check(o[:, :, heads], O, lse[:, heads], L, where=f"8-wave d={d} causal={causal} {mode}")
 
 
 @pytest.mark.parametrize("mode", ["online", "fixed_max"])
