@@ -42,10 +42,26 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff) {
 // HBM -> LDS without registers (buffer_load_dwordx4 ... lds): lane i's 16
 // bytes (from voff, zero when out of range) land at lds_wave + 16 * i, where
 // lds_wave is the same for the whole wave. Completion is counted by vmcnt.
+//
+// Issued from inline asm on purpose: the compiler cannot tell which LDS bytes
+// such a load writes once a read goes through the transposing-read builtin,
+// so with the builtin it waits for every load in flight (the next tile's)
+// before the current tile's V reads. Here it does not see the load at all;
+// the caller waits with wait_all_loads() before the barrier that publishes
+// the tile, and never reads LDS that a load in flight may write. The load
+// has no register result (no register of the asm is written later), and
+// s_nop gives the one wait state the hardware needs between the M0 write
+// and the load.
 __device__ __forceinline__ void buf_load_lds16(rsrc_t r, const void* lds_wave, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, (__attribute__((address_space(3))) void*)(lds_wave), 16, voff, 0, 0, 0);
+  const uint32_t m0v =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_wave;
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r),
+               "{m0}"(m0v)
+               : "memory");
 }
+// Waits until none of this wave's vector-memory loads is outstanding
+// (s_waitcnt vmcnt(0); the other counters are left alone).
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x70 | 0xF00); }
 
 // exp2 on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }

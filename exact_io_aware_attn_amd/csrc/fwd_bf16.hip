@@ -698,15 +698,20 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
   };
 
   const int n_steps = (n_tiles + KS - 1) / KS;
+  // each wave waits for its own tile loads, then the barrier publishes the
+  // tile to all waves (and frees the half that was just read)
   if (n_steps > 0) issue_tile(0, std::integral_constant<int, 0>());
+  wait_all_loads();
   __syncthreads();
   for (int st = 0; st < n_steps; st += 2) {
     if (st + 1 < n_steps) issue_tile(st + 1, std::integral_constant<int, 1>());
     tile_body(st, std::integral_constant<int, 0>());
+    wait_all_loads();
     __syncthreads();  // buffer set 0 free; step st+1 landed in set 1
     if (st + 1 < n_steps) {
       if (st + 2 < n_steps) issue_tile(st + 2, std::integral_constant<int, 0>());
       tile_body(st + 1, std::integral_constant<int, 1>());
+      wait_all_loads();
       __syncthreads();
     }
   }
