@@ -49,7 +49,7 @@ def library():
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_status_str.argtypes = [I]
     lib.attn_status_str.restype = ctypes.c_char_p
-    lib.attn_fwd_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.attn_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
     lib.attn_fwd_workspace_bytes.restype = Z
     lib.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, I, I, I,
                              ctypes.POINTER(_Strides), P, Z, P]
@@ -67,8 +67,9 @@ def attn_status_str(status):
     return library().attn_status_str(int(status)).decode()
 
 
-def attn_fwd_workspace_bytes(B, Hkv, Nk, d, softmax_mode):
-    return int(library().attn_fwd_workspace_bytes(B, Hkv, Nk, d, softmax_mode))
+def attn_fwd_workspace_bytes(B, Hkv, Nq, Nk, d, mask_kind, block_q, softmax_mode):
+    return int(library().attn_fwd_workspace_bytes(B, Hkv, Nq, Nk, d, mask_kind, block_q,
+                                                  softmax_mode))
 
 
 def attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d, kv_splits=0):
@@ -136,7 +137,7 @@ def _fwd_setup(q, k, v, causal, block_mask, block, scale, softmax, return_lse, o
     lse = None
     if return_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev) if lse_out is None else lse_out
-    need = attn_fwd_workspace_bytes(B, Hkv, Nk, d, mode)
+    need = attn_fwd_workspace_bytes(B, Hkv, Nq, Nk, d, mask_kind, bq, mode)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     st = (_Strides * 4)(_strides4(q), _strides4(k), _strides4(v), _strides4(o))

@@ -38,6 +38,13 @@ size_t fwd_ws(int B, int Hkv, int d, int mode) {
   return n;
 }
 
+// Segment table of a block mask whose block_q is not a multiple of 32
+// (placed after the fixed-max part of the workspace).
+size_t seg_ws(int Nq, int mask_kind, int block_q) {
+  if (!(mask_kind & MIATTN_MASK_BLOCK) || block_q <= 0 || block_q % 32 == 0) return 0;
+  return align_up(miattn::segment_table_bytes(Nq, block_q));
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool strides_ok(const miattn_strides& s, int64_t mult) {
@@ -88,10 +95,11 @@ const char* attn_status_str(int status) {
   }
 }
 
-size_t attn_fwd_workspace_bytes(int B, int Hkv, int Nk, int d, int softmax_mode) {
+size_t attn_fwd_workspace_bytes(int B, int Hkv, int Nq, int Nk, int d, int mask_kind,
+                                int block_q, int softmax_mode) {
   (void)Nk;
-  if (B < 0 || Hkv < 0 || d <= 0) return 0;
-  return fwd_ws(B, Hkv, d, softmax_mode);
+  if (B < 0 || Hkv < 0 || Nq < 0 || d <= 0) return 0;
+  return fwd_ws(B, Hkv, d, softmax_mode) + seg_ws(Nq, mask_kind, block_q);
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
@@ -145,7 +153,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if ((int64_t)Nk * sk.s * esz >= ((int64_t)1 << 31) || (int64_t)Nk * sv.s * esz >= ((int64_t)1 << 31))
     return MIATTN_ERR_UNSUPPORTED;
 
-  const size_t need = fwd_ws(B, Hkv, d, softmax_mode);
+  const size_t ks_bytes = fwd_ws(B, Hkv, d, softmax_mode);
+  const size_t need = ks_bytes + seg_ws(Nq, mask_kind, block_q);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MIATTN_ERR_WORKSPACE;
 
   hipStream_t s = (hipStream_t)stream;
@@ -163,6 +172,14 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   p.block_q = block_q; p.block_k = block_k; p.nkb = nkb;
   // with no keys every row is empty and there is nothing to bound
   p.fixed = Nk > 0 ? softmax_mode : MIATTN_SOFTMAX_ONLINE;
+
+  // the bf16 kernel takes the rows of such a mask in segments of identical
+  // mask rows (the fp32 kernel works per block row)
+  if (block && block_q % 32 != 0 && dtype == MIATTN_BF16) {
+    if (miattn::launch_segments(block_mask, Nq, block_q, nkb, (char*)workspace + ks_bytes,
+                                &p.segs, s) != hipSuccess)
+      return MIATTN_ERR_HIP;
+  }
 
   if (p.fixed != MIATTN_SOFTMAX_ONLINE) {
     const size_t bh = (size_t)B * Hkv;

@@ -155,21 +155,24 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
   const int hq = hkv * G + g;
 
   // ---- rows of this wave. A block mask whose block_q is not a multiple of 32
-  // cuts the rows into segments that never cross a block row (32, 32, ...,
-  // the rest, per block row; lanes past a short segment hold no query), so
-  // every wave lies in one block row and can skip the key groups dead for it
-  // outright: a dead key is then never multiplied into any of the wave's rows.
+  // cuts the rows into segments of at most 32 rows that never mix block rows
+  // whose mask rows differ (from the segment table: runs of identical mask
+  // rows, cut into 32-row pieces; lanes past a short segment hold no query),
+  // so all rows of a wave see the same keys and the wave can skip the key
+  // groups dead for it outright: a dead key is then never multiplied into
+  // any of the wave's rows. The grid is sized for the segment count without
+  // merging; workgroups past the last segment have nothing to do.
   int q_start, q_end, q0, nrows;
   if (BLOCK && p.block_q % 32 != 0) {
-    const int spb = (p.block_q + 31) / 32;  // segments per block row
-    const int nseg = (p.Nq / p.block_q) * spb;
+    const int nseg = *p.segs.count;
     const int s0 = qt * NW, sw = s0 + wave;
-    const int brow = sw / spb;
-    q0 = sw < nseg ? brow * p.block_q + (sw - brow * spb) * 32 : p.Nq;
-    nrows = sw < nseg ? min(32, p.block_q - (sw - brow * spb) * 32) : 0;
-    const int s1 = min(s0 + NW, nseg) - 1;  // last segment of the workgroup
-    q_start = (s0 / spb) * p.block_q;
-    q_end = min(p.Nq, (s1 / spb + 1) * p.block_q);
+    if (s0 >= nseg) return;  // the same for every wave of the workgroup
+    const int2 sg = sw < nseg ? p.segs.seg[sw] : make_int2(p.Nq, 0);
+    q0 = sg.x;
+    nrows = sg.y;
+    const int2 last = p.segs.seg[min(s0 + NW, nseg) - 1];
+    q_start = p.segs.seg[s0].x;
+    q_end = last.x + last.y;
   } else {
     q_start = qt * BQ;
     q_end = min(q_start + BQ, p.Nq);

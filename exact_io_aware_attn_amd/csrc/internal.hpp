@@ -12,6 +12,14 @@ namespace miattn {
 constexpr int kMaxSplit = 64;
 constexpr int kMaxLiveBlocks = 4096;
 
+// Row segments of a block mask with block_q not a multiple of 32 (built by
+// launch_segments): seg[s] = {first query row, rows (1..32)} in row order,
+// *count of them; no segment mixes block rows whose mask rows differ.
+struct SegTable {
+  const int* count;
+  const int2* seg;
+};
+
 struct KStats {
   const float* part_max;  // [B*Hkv][kMaxSplit], max |k|^2 or |k - kbar|^2
   const float* kbar;      // [B*Hkv][d] mean key (centred mode) or nullptr
@@ -34,6 +42,7 @@ struct FwdParams {
   int causal_off;     // Nk - Nq: key j visible to row i iff j <= i + causal_off
   const uint8_t* block_mask;
   int block_q, block_k, nkb;  // nkb = Nk / block_k
+  SegTable segs;              // block masks with block_q % 32 != 0
   int fixed;          // 0 online, 1 fixed max, 2 fixed max with centred keys
   KStats ks;
   int n_qtiles;
@@ -75,5 +84,12 @@ hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, bool block,
 hipError_t launch_kstats(const KStatParams& p, int d, bool bf16, bool centred,
                          hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t s);
+
+inline int64_t align16(int64_t n) { return (n + 15) & ~(int64_t)15; }
+// workspace bytes of the segment table of an Nq-row mask with block_q rows per block
+size_t segment_table_bytes(int Nq, int block_q);
+// builds the table in ws (segment_table_bytes(Nq, block_q) bytes) on stream s
+hipError_t launch_segments(const uint8_t* block_mask, int Nq, int block_q, int nkb, void* ws,
+                           SegTable* out, hipStream_t s);
 
 }  // namespace miattn

@@ -76,8 +76,15 @@ typedef struct {
   int64_t b, s, h;
 } miattn_strides;
 
-/* Bytes of device workspace attn_fwd needs (0 for ONLINE). */
-size_t attn_fwd_workspace_bytes(int B, int Hkv, int Nk, int d, int softmax_mode);
+/* Bytes of device workspace attn_fwd needs for these arguments (the same
+ * meaning as in attn_fwd; block_q is read only when mask_kind has BLOCK).
+ * Nonzero for the fixed-max modes (per-(batch, KV head) key statistics) and
+ * for a BLOCK mask whose block_q is not a multiple of 32 (a table of row
+ * segments: runs of block rows with identical mask rows, cut into pieces of
+ * at most 32 rows, built on the stream before the attention kernel). Zero
+ * otherwise. Returns 0 for negative sizes. */
+size_t attn_fwd_workspace_bytes(int B, int Hkv, int Nq, int Nk, int d, int mask_kind,
+                                int block_q, int softmax_mode);
 
 /* Prefill / full-sequence attention.
  *
@@ -101,8 +108,10 @@ size_t attn_fwd_workspace_bytes(int B, int Hkv, int Nk, int d, int softmax_mode)
  * softmax_mode  MIATTN_SOFTMAX_*
  * strides  NULL (packed) or an array of 4: q, k, v, o
  * workspace, workspace_bytes  device scratch of at least
- *        attn_fwd_workspace_bytes(B, Hkv, Nk, d, softmax_mode) bytes
- *        (may be NULL / 0 for ONLINE)
+ *        attn_fwd_workspace_bytes(B, Hkv, Nq, Nk, d, mask_kind, block_q,
+ *        softmax_mode) bytes (may be NULL / 0 when that is 0); owned by the
+ *        caller, overwritten by the call, free for reuse once the call's work
+ *        on the stream has finished
  * stream   hipStream_t
  * A query row with no visible key yields O = 0 and LSE = -inf. Positions a
  * mask excludes never influence the result, whatever their values. */

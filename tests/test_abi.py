@@ -42,10 +42,19 @@ def test_status_strings():
 
 
 def test_workspace_sizes():
-    assert bd.attn_fwd_workspace_bytes(1, 24, 14080, 128, 0) == 0
-    plain = bd.attn_fwd_workspace_bytes(1, 24, 14080, 128, 1)
-    centred = bd.attn_fwd_workspace_bytes(1, 24, 14080, 128, 2)
+    NONE, CAUSAL, BLOCK = bd.MIATTN_MASK_NONE, bd.MIATTN_MASK_CAUSAL, bd.MIATTN_MASK_BLOCK
+    assert bd.attn_fwd_workspace_bytes(1, 24, 14080, 14080, 128, NONE, 0, 0) == 0
+    assert bd.attn_fwd_workspace_bytes(1, 24, 14080, 14080, 128, CAUSAL, 80, 0) == 0
+    plain = bd.attn_fwd_workspace_bytes(1, 24, 14080, 14080, 128, NONE, 0, 1)
+    centred = bd.attn_fwd_workspace_bytes(1, 24, 14080, 14080, 128, NONE, 0, 2)
     assert plain >= 24 * 64 * 4 and centred > plain
+    # block masks with block_q not a multiple of 32 carry a row-segment table:
+    # 176 block rows of 80 -> at most 3 segments each, 8 bytes per segment
+    seg = bd.attn_fwd_workspace_bytes(1, 24, 14080, 14080, 128, BLOCK, 80, 0)
+    assert seg >= 176 + 176 * 3 * 8
+    assert bd.attn_fwd_workspace_bytes(1, 24, 14080, 14080, 128, BLOCK, 64, 0) == 0
+    assert bd.attn_fwd_workspace_bytes(1, 24, 14080, 14080, 128, BLOCK | CAUSAL, 80, 1) >= plain + seg
+    assert bd.attn_fwd_workspace_bytes(-1, 24, 14080, 14080, 128, BLOCK, 80, 1) == 0
     ws = bd.attn_decode_workspace_bytes(64, 32, 8, 32768, 128, 0)
     assert ws >= (4096 + 64) * 32 * 129 * 4
     assert ws == bd.attn_decode_workspace_bytes(64, 32, 8, 100, 128, 17)
@@ -71,6 +80,8 @@ def _fwd(**kw):
     (dict(mask_kind=2, block_mask=16, block_q=48, block_k=16), 2),
     (dict(mask_kind=2, block_mask=None, block_q=16, block_k=16), 1),
     (dict(mode=1), 4), (dict(q=18), 3),
+    # block_q not a multiple of 32: the row-segment table needs workspace
+    (dict(mask_kind=2, block_mask=16, block_q=16, block_k=16), 4),
     (dict(B=0), 0), (dict(Nq=0), 0),
 ])
 def test_fwd_validation(kw, status):

@@ -164,6 +164,54 @@ def test_bf16_random_block_mask(bq, bk, causal):
     check(o, O, lse, L, where=f"block {bq}x{bk} causal={causal}")
 
 
+def _runs_mask(rng, nqb, nkb, max_run):
+    """Block mask whose rows come in runs of identical rows (1..max_run long),
+    each run with its own random row; every run sees at least one block."""
+    rows, lens = [], []
+    while len(rows) < nqb:
+        n = min(int(rng.integers(1, max_run + 1)), nqb - len(rows))
+        r = (rng.random(nkb) < 0.5).astype(np.uint8)
+        r[int(rng.integers(0, nkb))] = 1
+        rows += [r] * n
+        lens.append(n)
+    return np.stack(rows), lens
+
+
+@pytest.mark.parametrize("mode", ["online", "fixed_max"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bq,bk", [(16, 32), (48, 16), (80, 80)])
+def test_bf16_block_mask_runs_of_identical_rows(bq, bk, causal, mode):
+    """Block rows with identical mask rows share 32-row segments (a segment
+    may span two or three block rows of one run, never two runs): runs of
+    1..4 block rows, so segments end mid-block-row and runs end mid-segment.
+    Every row against the oracle."""
+    rng = np.random.default_rng(bq * 7 + bk + causal)
+    nqb = max(1536 // bq, 30)
+    nkb = 6 * 80 // bk
+    bm, lens = _runs_mask(rng, nqb, nkb, 4)
+    assert len(lens) > 5 and max(lens) > 1
+    Nq, Nk = nqb * bq, nkb * bk
+    q, k, v = prefill_inputs(1, 4, 2, Nq, Nk, 128, torch.bfloat16, seed=bq + bk)
+    o, lse = _run(q, k, v, causal=causal, block_mask=bm, block=(bq, bk), softmax=mode)
+    O, L = _ref(q, k, v, 1 / math.sqrt(128), causal=causal, block_mask=bm, block_q=bq, block_k=bk)
+    check(o, O, lse, L, where=f"runs {bq}x{bk} causal={causal} {mode}")
+
+
+@pytest.mark.parametrize("bq", [48, 80])
+def test_bf16_block_mask_runs_eight_wave(bq):
+    """The same with enough (batch, head) pairs for 8-wave workgroups, which
+    may span the end of one run and the start of the next."""
+    rng = np.random.default_rng(bq)
+    nqb, nkb = 960 // bq, 12
+    bm, _ = _runs_mask(rng, nqb, nkb, 4)
+    Nq, Nk = nqb * bq, nkb * 64
+    q, k, v = prefill_inputs(16, 16, 4, Nq, Nk, 64, torch.bfloat16, seed=bq)
+    o, lse = _run(q, k, v, block_mask=bm, block=(bq, 64))
+    heads = [0, 9, 15]
+    O, L = _ref(q[:2], k[:2], v[:2], 1 / 8, block_mask=bm, block_q=bq, block_k=64, heads=heads)
+    check(o[:2][:, :, heads], O, lse[:2][:, heads], L, where=f"runs 8-wave bq={bq}")
+
+
 def test_f32_block_mask():
     rng = np.random.default_rng(3)
     bm = (rng.random((6, 5)) < 0.5).astype(np.uint8)
