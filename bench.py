@@ -16,10 +16,13 @@ Printed (one JSON line):
   roofline   prefill kernel against the dense bf16 MFMA peak
   roofline_decode  decode against the HBM peak
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample
+  ms_parts_back_to_back  per part, the average of --back-to-back calls (200)
+             issued back to back after the timed steps (warm, no host gaps)
 
 --workload runs a single named workload instead (one call per step):
-gpt2-causal, llama3-8b-gqa-causal-8k, gqa-decode-b64, video-frames-16x880
-(online), video-frames-16x880-fixed, video-frames-16x880-centered, tiny-f32.
+gpt2-causal, gpt2-medium-causal, llama3-8b-gqa-causal-8k, gqa-decode-b64,
+video-frames-16x880 (online), video-frames-16x880-fixed,
+video-frames-16x880-centered, tiny-f32.
 """
 
 import argparse
@@ -68,6 +71,9 @@ def parse():
     ap.add_argument("--workload", default="default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--back-to-back", type=int, default=200,
+                    help="after the timed steps, time this many calls of each part back "
+                         "to back between one pair of events (ms_parts_back_to_back)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before the steps, copy this many MiB device-to-device once "
                          "(a plain copy of known size that scales HBM byte counters)")
@@ -211,6 +217,17 @@ def main():
     wall = time.perf_counter() - t0
     ms = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
           for i in range(len(parts))]
+    # after the timed steps: each part's average over back-to-back calls
+    # between one pair of events (warm; no gap for the host between calls)
+    b2b = {}
+    for p in parts:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.back_to_back):
+            p.call()
+        e1.record()
+        torch.cuda.synchronize()
+        b2b[p.name] = e0.elapsed_time(e1) / max(args.back_to_back, 1)
     ms_avg = [sum(m) / len(m) for m in ms]
     ms_step = wall * 1e3 / args.steps
 
@@ -244,6 +261,7 @@ def main():
     # per-call spread over the timed steps (warm: inputs resident, GPU clocks up)
     out["ms_parts_median"] = {p.name: sorted(m)[len(m) // 2] for p, m in zip(parts, ms)}
     out["ms_parts_min"] = {p.name: min(m) for p, m in zip(parts, ms)}
+    out["ms_parts_back_to_back"] = b2b
     out["roofline"] = roof
     if len(parts) > 1 and parts[1].kind == "decode":
         d = parts[1]

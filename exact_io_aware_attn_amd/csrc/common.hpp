@@ -52,10 +52,27 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff) {
 // has no register result (no register of the asm is written later), and
 // s_nop gives the one wait state the hardware needs between the M0 write
 // and the load.
-__device__ __forceinline__ void buf_load_lds16(rsrc_t r, const void* lds_wave, uint32_t voff) {
-  const uint32_t m0v =
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_wave;
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r),
+//
+// The asm takes the buffer resource as four dwords in scalar registers (the
+// same words make_rsrc builds: base, base_hi | stride 0, size, flags), each
+// read from the first lane: the values are uniform, and this keeps the
+// operand in SGPRs whatever the compiler can prove about them.
+struct DmaRsrc {
+  u32x4 w;
+};
+__device__ __forceinline__ DmaRsrc dma_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  DmaRsrc r;
+  r.w[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r.w[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  r.w[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r.w[3] = 0x00020000u;
+  return r;
+}
+__device__ __forceinline__ void buf_load_lds16(DmaRsrc r, const void* lds_wave, uint32_t voff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_wave);
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r.w),
                "{m0}"(m0v)
                : "memory");
 }

@@ -300,8 +300,8 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
     return n > 0 ? (uint32_t)(((int64_t)(n - 1) * stride + D) * 2) : 0u;
   };
   // BLOCK: one resource over all Nk rows, rows gathered by key index
-  const rsrc_t rk_all = make_rsrc(kg, span(p.Nk, p.k_ss));
-  const rsrc_t rv_all = make_rsrc(vg, span(p.Nk, p.v_ss));
+  const DmaRsrc rk_all = dma_rsrc(kg, span(p.Nk, p.k_ss));
+  const DmaRsrc rv_all = dma_rsrc(vg, span(p.Nk, p.v_ss));
   // step st loads tiles st * KS + k, k < KS (tiles past the end read as
   // zeros: their range is empty)
   auto issue_tile = [&](int st, auto bufc) {
@@ -313,8 +313,8 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
         __bf16* const dv = sVb[BUF * KS + k];
         const int r0 = (st * KS + k) * BK;
         const int nvalid = min(BK, kv_end - r0);
-        const rsrc_t rk = make_rsrc(kg + (int64_t)r0 * p.k_ss, span(nvalid, p.k_ss));
-        const rsrc_t rv = make_rsrc(vg + (int64_t)r0 * p.v_ss, span(nvalid, p.v_ss));
+        const DmaRsrc rk = dma_rsrc(kg + (int64_t)r0 * p.k_ss, span(nvalid, p.k_ss));
+        const DmaRsrc rv = dma_rsrc(vg + (int64_t)r0 * p.v_ss, span(nvalid, p.v_ss));
 #pragma unroll
         for (int j = 0; j < NIW; ++j) {
           const int lds_row = (wave * NIW + j) * RPI;

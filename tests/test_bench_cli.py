@@ -23,7 +23,8 @@ def test_more_than_one_gpu_is_refused():
 def test_help_lists_the_contract_flags():
     r = _run("--help")
     assert r.returncode == 0
-    for flag in ("--gpus", "--steps", "--warmup", "--workload", "--no-cpu-baseline"):
+    for flag in ("--gpus", "--steps", "--warmup", "--workload", "--no-cpu-baseline",
+                 "--back-to-back"):
         assert flag in r.stdout
 
 
