@@ -49,9 +49,13 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff) {
 // before the current tile's V reads. Here it does not see the load at all;
 // the caller waits with wait_all_loads() before the barrier that publishes
 // the tile, and never reads LDS that a load in flight may write. The load
-// has no register result (no register of the asm is written later), and
-// s_nop gives the one wait state the hardware needs between the M0 write
-// and the load.
+// has no register result (no register of the asm is written later).
+//
+// Wait states: the compiler inserts none for an instruction inside inline
+// asm, so the asm starts with s_nop 4 (five wait states). A vector-memory
+// instruction that reads an SGPR written by a VALU instruction (the
+// descriptor words below come from v_readfirstlane) needs five, and the
+// LDS-DMA read of M0 after an SALU write of M0 needs one.
 //
 // The asm takes the buffer resource as four dwords in scalar registers (the
 // same words make_rsrc builds: base, base_hi | stride 0, size, flags), each
@@ -72,7 +76,7 @@ __device__ __forceinline__ DmaRsrc dma_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ void buf_load_lds16(DmaRsrc r, const void* lds_wave, uint32_t voff) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_wave);
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r.w),
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r.w),
                "{m0}"(m0v)
                : "memory");
 }
