@@ -3,9 +3,11 @@
 // Same method as the bf16 kernel -- keys streamed in tiles through LDS, a
 // running row max and sum per query, the output rescaled when the max grows
 // ("Attention Mechanism Optimization for Efficient LLM Inference",
-// "Online-Softmax") -- but on the vector ALU: one lane per query row, 64 rows
-// per workgroup, K/V tiles of 32 keys in LDS. This is the accuracy path for
-// fp32 inputs; it is not the throughput path.
+// "Online-Softmax") -- but on the vector ALU: 16 lanes per query row, each
+// holding a 1/16 slice of d for q and O (a score is a partial dot product
+// summed over the row's lanes), 16 rows per workgroup of 4 waves, K/V tiles
+// of 32 keys in LDS. This is the accuracy path for fp32 inputs; it is not
+// the throughput path.
 //
 // Masked pairs are excluded by selection, not by multiplying with zero, so a
 // non-finite value at an excluded position never reaches the output.
@@ -17,63 +19,82 @@ namespace miattn {
 
 namespace {
 
-constexpr int BQ = 64;
-constexpr int TK = 32;
+constexpr int LPR = 16;           // lanes per query row (each holds D / 16 of d)
+constexpr int RPW = 64 / LPR;     // query rows per wave
+constexpr int NWF = 4;            // waves per workgroup
+constexpr int BQ = RPW * NWF;     // query rows per workgroup
+constexpr int TK = 32;            // keys per LDS tile
+
+// sum over the LPR lanes of one query row (lane ids differ in the low bits)
+__device__ __forceinline__ float row_sum(float v) {
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) v += shfl_xor(v, m);
+  return v;
+}
 
 template <int D, bool CAUSAL, bool BLOCK>
-__global__ void __launch_bounds__(BQ) fwd_f32_kernel(const FwdParams p) {
-  __shared__ float sK[TK][D];
-  __shared__ float sV[TK][D];
-  __shared__ __attribute__((aligned(16))) float sQ[BQ][D + 4];  // this lane's query row
+__global__ void __launch_bounds__(64 * NWF) fwd_f32_kernel(const FwdParams p) {
+  constexpr int DL = D / LPR;  // elements of d per lane
+  __shared__ __attribute__((aligned(16))) float sK[TK][D];
+  __shared__ __attribute__((aligned(16))) float sV[TK][D];
 
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int d0 = (tid % LPR) * DL;  // this lane's slice of d
   const int qt = blockIdx.x;
   const int bh = blockIdx.y;
   const int b = bh / p.Hq, hq = bh - b * p.Hq;
   const int hkv = hq / (p.Hq / p.Hkv);
-  const int lane = threadIdx.x;
-  const int qrow = qt * BQ + lane;
+  const int qrow = qt * BQ + tid / LPR;
   const bool row_ok = qrow < p.Nq;
 
-  float o[D];
-  float* q = sQ[lane];
+  float q[DL], o[DL];
   {
-    const float* qp = (const float*)p.q + b * p.q_sb + (int64_t)(row_ok ? qrow : 0) * p.q_ss + hq * p.q_sh;
+    const float* qp = (const float*)p.q + b * p.q_sb + (int64_t)(row_ok ? qrow : 0) * p.q_ss +
+                      hq * p.q_sh + d0;
 #pragma unroll
-    for (int d = 0; d < D; d += 4)
-      *(float4*)(q + d) = row_ok ? *(const float4*)(qp + d) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < DL; i += 4) {
+      const float4 x = row_ok ? *(const float4*)(qp + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      q[i] = x.x;
+      q[i + 1] = x.y;
+      q[i + 2] = x.z;
+      q[i + 3] = x.w;
+    }
 #pragma unroll
-    for (int d = 0; d < D; ++d) o[d] = 0.f;
+    for (int i = 0; i < DL; ++i) o[i] = 0.f;
   }
   const float* kg = (const float*)p.k + b * p.k_sb + hkv * p.k_sh;
   const float* vg = (const float*)p.v + b * p.v_sb + hkv * p.v_sh;
 
-  // fixed-max bound, and eligibility per group of 32 rows (each half-wave),
-  // the same rule as the bf16 kernel's
+  // fixed-max bound, and eligibility per wave (its RPW rows), the same rule
+  // as the bf16 kernel's
   bool fixed = false;
   float m_fix = 0.f;
   if (p.fixed) {
     float qq = 0.f, qk = 0.f;
 #pragma unroll
-    for (int d = 0; d < D; ++d) qq += q[d] * q[d];
+    for (int i = 0; i < DL; ++i) qq += q[i] * q[i];
+    qq = row_sum(qq);
     const int64_t bk = (int64_t)b * p.Hkv + hkv;
     float r2 = lane < p.ks.nsplit ? p.ks.part_max[bk * kMaxSplit + lane] : 0.f;
     r2 = wave_max(r2);
     const float rho = sqrtf(r2);
-    if (p.fixed == 2)
-      for (int d = 0; d < D; ++d) qk += q[d] * p.ks.kbar[bk * D + d];
+    if (p.fixed == 2) {
+#pragma unroll
+      for (int i = 0; i < DL; ++i) qk += q[i] * p.ks.kbar[bk * D + d0 + i];
+      qk = row_sum(qk);
+    }
     const float qn = sqrtf(qq);
     m_fix = p.scale * (qk + qn * rho) * kLog2e;
-    float gap = row_ok ? 2.f * p.scale * qn * rho : 0.f;
-#pragma unroll
-    for (int m = 16; m >= 1; m >>= 1) gap = fmaxf(gap, shfl_xor(gap, m));
-    fixed = gap <= kTau;
+    const float gap = row_ok ? 2.f * p.scale * qn * rho : 0.f;
+    fixed = wave_max(gap) <= kTau;
   }
 
   float m_run = kNegInf, l_run = 0.f;
   const int my_qb = BLOCK ? (row_ok ? qrow : 0) / p.block_q : 0;
   for (int k0 = 0; k0 < p.Nk; k0 += TK) {
     __syncthreads();
-    for (int i = lane; i < TK * D / 4; i += BQ) {
+    for (int i = tid; i < TK * D / 4; i += 64 * NWF) {
       const int r = (i * 4) / D, d = (i * 4) - r * D;
       const int key = k0 + r;
       float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
@@ -93,17 +114,19 @@ __global__ void __launch_bounds__(BQ) fwd_f32_kernel(const FwdParams p) {
       const int key = k0 + 16 * gi;
       grp[gi] = !BLOCK || (key < p.Nk && p.block_mask[(int64_t)my_qb * p.nkb + key / p.block_k] != 0);
     }
-    // excluded pairs carry -inf and are skipped below
+    // scores of the tile: each lane's partial dot product over its slice of
+    // d, summed over the row's lanes; excluded pairs carry -inf
     float s[TK];
     float mx = kNegInf;
-#pragma unroll 1
+#pragma unroll
     for (int j = 0; j < TK; ++j) {
       const int key = k0 + j;
       bool a = key < p.Nk && row_ok && grp[j / 16];
       if (CAUSAL) a = a && key <= qrow + p.causal_off;
       float acc = 0.f;
 #pragma unroll
-      for (int d = 0; d < D; ++d) acc = fmaf(q[d], sK[j][d], acc);
+      for (int i = 0; i < DL; ++i) acc = fmaf(q[i], sK[j][d0 + i], acc);
+      acc = row_sum(acc);
       s[j] = a ? acc * p.scale_log2 : kNegInf;
       mx = fmaxf(mx, s[j]);
     }
@@ -115,17 +138,18 @@ __global__ void __launch_bounds__(BQ) fwd_f32_kernel(const FwdParams p) {
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int d = 0; d < D; ++d) o[d] *= alpha;
+      for (int i = 0; i < DL; ++i) o[i] *= alpha;
     } else {
       m_ref = m_fix;
     }
-#pragma unroll 1
+    // excluded pairs are skipped, never multiplied by zero
+#pragma unroll
     for (int j = 0; j < TK; ++j) {
       if (s[j] != kNegInf) {
         const float e = ex2(s[j] - m_ref);
         l_run += e;
 #pragma unroll
-        for (int d = 0; d < D; ++d) o[d] = fmaf(e, sV[j][d], o[d]);
+        for (int i = 0; i < DL; ++i) o[i] = fmaf(e, sV[j][d0 + i], o[i]);
       }
     }
   }
@@ -133,11 +157,11 @@ __global__ void __launch_bounds__(BQ) fwd_f32_kernel(const FwdParams p) {
   if (row_ok) {
     const bool live = l_run > 0.f;
     const float inv = live ? 1.f / l_run : 0.f;
-    float* op = (float*)p.o + b * p.o_sb + (int64_t)qrow * p.o_ss + hq * p.o_sh;
+    float* op = (float*)p.o + b * p.o_sb + (int64_t)qrow * p.o_ss + hq * p.o_sh + d0;
 #pragma unroll
-    for (int d = 0; d < D; d += 4)
-      *(float4*)(op + d) = make_float4(o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv);
-    if (p.lse != nullptr) {
+    for (int i = 0; i < DL; i += 4)
+      *(float4*)(op + i) = make_float4(o[i] * inv, o[i + 1] * inv, o[i + 2] * inv, o[i + 3] * inv);
+    if (p.lse != nullptr && d0 == 0) {
       const float m_ref = fixed ? m_fix : m_run;
       p.lse[((int64_t)b * p.Hq + hq) * p.Nq + qrow] = live ? (m_ref + log2f(l_run)) * kLn2 : kNegInf;
     }
@@ -147,7 +171,7 @@ __global__ void __launch_bounds__(BQ) fwd_f32_kernel(const FwdParams p) {
 template <int D, bool C, bool K>
 hipError_t launch_one(const FwdParams& p, hipStream_t s) {
   const dim3 grid((p.Nq + BQ - 1) / BQ, p.B * p.Hq);
-  hipLaunchKernelGGL((fwd_f32_kernel<D, C, K>), grid, dim3(BQ), 0, s, p);
+  hipLaunchKernelGGL((fwd_f32_kernel<D, C, K>), grid, dim3(64 * NWF), 0, s, p);
   return hipGetLastError();
 }
 
