@@ -109,7 +109,10 @@ __device__ __forceinline__ void map_workgroup(int i, int G, int nX, int& X, int&
 // weights it was accumulated with (exact for a single visible key, where the
 // bound leaves P well below 1 and its rounding would otherwise show), and
 // the LSE uses the fp32 sum.
-template <int D, bool CAUSAL, bool BLOCK, int NW, int KS = 1, bool FX = false>
+// HP: the second half of the causal row blocks (the heavier ones) issues one
+// priority step above the first half; used when every workgroup is resident
+// at once, so the kernel ends with the heaviest ones.
+template <int D, bool CAUSAL, bool BLOCK, int NW, int KS = 1, bool FX = false, bool HP = false>
 // waves per SIMD asked of the register allocator. d = 64 with 4 waves and
 // whole rows: three (<= 170 VGPRs, 32 KiB of LDS per workgroup, three
 // workgroups per CU). d = 64 dense with 8 waves: four (128 VGPRs, two
@@ -153,6 +156,8 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
   const int qt_rank = t2 / p.B;
   const int qt = CAUSAL ? (p.n_qtiles - 1 - qt_rank) : qt_rank;
   const int hq = hkv * G + g;
+  static_assert(!HP || (CAUSAL && !BLOCK && KS == 1), "priority boost: dense causal whole rows");
+  const bool prio = HP && 2 * qt >= p.n_qtiles;
 
   // ---- rows of this wave. A block mask whose block_q is not a multiple of 32
   // cuts the rows into segments of at most 32 rows that never mix block rows
@@ -600,7 +605,8 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
     // by stage): of the two waves sharing a SIMD, the one further behind is
     // served first, so they reach the tile's barrier closer together.
     auto body_fast = [&]() __attribute__((always_inline)) {
-      __builtin_amdgcn_s_setprio(2);
+      if (HP && prio) __builtin_amdgcn_s_setprio(3);
+      else __builtin_amdgcn_s_setprio(2);
       // ---- stage 1: S^T block 0, then block 1 with block 0's softmax
       constexpr int NK = 2 * KSTEPS;   // K fragments per tile
       constexpr int LEAD = 3;          // K fragments in flight
@@ -643,7 +649,8 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
       float lb0 = P0.l0 + P0.l1;
       f32x16 e0 = P0.e;
       fence();
-      __builtin_amdgcn_s_setprio(1);
+      if (HP && prio) __builtin_amdgcn_s_setprio(2);
+      else __builtin_amdgcn_s_setprio(1);
       settle(s[0], e0, lb0);
       // ---- stage 2: PV of block 0 with block 1's softmax
       const float m1 = fixed ? m_fix : m_run;
@@ -678,7 +685,8 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
       float lb1 = P1.l0 + P1.l1;
       f32x16 e1 = P1.e;
       fence();
-      __builtin_amdgcn_s_setprio(0);
+      if (HP && prio) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
       settle(s[1], e1, lb1);
       // ---- stage 3: PV of block 1
       pf[0] = cvt8(e1[0], e1[1], e1[2], e1[3], e1[4], e1[5], e1[6], e1[7]);
@@ -812,8 +820,18 @@ hipError_t launch_one(const FwdParams& p0, hipStream_t s) {
                          dim3(p.n_qtiles * p.B * p.Hq), dim3(256), 0, s, p);
   } else {
     p.n_qtiles = seg ? (nseg + 3) / 4 : (p.Nq + 127) / 128;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BLOCK, 4, 1, FX>),
-                       dim3(p.n_qtiles * p.B * p.Hq), dim3(256), 0, s, p);
+    const int64_t nwg = (int64_t)p.n_qtiles * p.B * p.Hq;
+    if constexpr (D == 64 && CAUSAL && !BLOCK) {
+      // all workgroups resident at once (three per CU): boost the heavy half
+      int dev = 0, ncu = 0;
+      if (hipGetDevice(&dev) == hipSuccess &&
+          hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+          nwg <= 3 * (int64_t)ncu) {
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BLOCK, 4, 1, FX, true>), dim3(nwg), dim3(256), 0, s, p);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, BLOCK, 4, 1, FX>), dim3(nwg), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }
