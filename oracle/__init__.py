@@ -17,18 +17,24 @@ What it computes (each function cites the page passage it follows):
                         row maximum (equal to ``attention`` in exact arithmetic).
 * ``online_softmax``  -- the running (max, sum) recurrence over blocks of a row.
 * ``merge_partials``  -- combining (O, LSE) pairs of disjoint key sets.
+* ``attention_backward`` -- dQ, dK, dV of the same function for an upstream
+                        gradient dO (chain rule through S, P and the softmax).
 
 Pins (tests/test_oracle.py): printed worked examples (tests/golden/), closed
 forms (single key, identical keys, causal first row), invariants (row sums,
 joint permutation, shift invariance, split == unsplit), library routines
 (torch SDPA in float64 on the CPU, scipy logsumexp) and an independent
-frame-gather construction for block masks.
+frame-gather construction for block masks. The gradients are pinned to
+central finite differences of the forward oracle, to closed forms (constant V,
+a single key), to invariants (key-shift invariance, value-gradient sums) and to
+torch autograd in float64 on the CPU (tests/test_oracle_backward.py).
 
 Parity unpinned: the eligibility threshold ``TAU`` = 64 is a constant chosen
 here from an underflow argument, not a value the pages give; only the rule's
 soundness (the normaliser stays far above the fp32 minimum) is tested.
 """
 
+from .backward import attention_backward  # noqa: F401
 from .attention import (  # noqa: F401
     TAU,
     attention,

@@ -1,0 +1,82 @@
+"""fp64 reference gradients of exact attention, written out from the definition.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): nothing on the product
+path imports this module.
+
+Pages cited (by title and section):
+
+* "플래시어텐션: 메모리를 아끼는 정확한 어텐션" (FlashAttention explainer,
+  base.kaita.kr): §4 재계산 -- the backward pass keeps only O and the row
+  statistics from the forward pass and rebuilds S and P from Q, K, V; the
+  algorithm flowchart ends in the same step; FAQ item 3 restates it.
+* "Attention Mechanism Optimization for Efficient LLM Inference"
+  (pyy0715.github.io): "Background: Scaled Dot-Product Attention" (the function
+  being differentiated) and "Grouped-Query Attention (GQA)" (query heads of a
+  group share one K/V head).
+
+The pages give the recomputation principle but print no gradient formulas.
+Reading taken here: the backward pass returns the exact gradient of
+O = softmax(scale * Q K^T + mask) V with respect to Q, K and V, for an upstream
+gradient dO, by the chain rule; nothing else is plausible for an exact method.
+With GQA a K/V head's gradient is the sum over the query heads that read it.
+Masked pairs have P = 0 and receive no gradient.
+"""
+
+import numpy as np
+
+from .attention import _check_heads, element_mask
+
+_ROW_CHUNK = 2048
+
+
+def attention_backward(q, k, v, do, scale, *, causal=False, block_mask=None,
+                       block_q=None, block_k=None):
+    """Gradients (dQ, dK, dV) of exact attention, fp64.
+
+    q, do: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d]. Returns dQ [B, Nq, Hq, d],
+    dK and dV [B, Nk, Hkv, d], all float64.
+
+    Per batch b and query head h (K/V head h // (Hq / Hkv)):
+    1. S = scale * Q K^T with -inf at disallowed pairs; P = softmax(S) per row,
+       the same safe softmax as the forward oracle. A row with no allowed key
+       has P = 0 (its output is the constant 0).
+    2. O = P V is linear in P and in V:  dV = P^T dO  and  dP = dO V^T.
+    3. Softmax Jacobian per row: dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik).
+    4. S is linear in Q and K:  dQ = scale * dS K  and  dK = scale * dS^T Q.
+    5. GQA: dK and dV of a K/V head accumulate over its query heads.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, Nq, Hq, d = q.shape
+    Bk, Nk, Hkv, dk = k.shape
+    if Bk != B or dk != d or v.shape != k.shape or do.shape != q.shape:
+        raise ValueError("q/k/v/do shapes do not agree")
+    group = _check_heads(Hq, Hkv)
+
+    dQ = np.zeros_like(q)
+    dK = np.zeros_like(k)
+    dV = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            kvh = h // group
+            Kb = k[b, :, kvh, :]
+            Vb = v[b, :, kvh, :]
+            for r0 in range(0, Nq, _ROW_CHUNK):
+                rr = np.arange(r0, min(Nq, r0 + _ROW_CHUNK))
+                allowed = element_mask(Nq, Nk, causal=causal, block_mask=block_mask,
+                                       block_q=block_q, block_k=block_k, rows=rr)
+                S = np.where(allowed, scale * (q[b, rr, h, :] @ Kb.T), -np.inf)
+                live = allowed.any(axis=1)
+                m = np.where(live, S.max(axis=1), 0.0)
+                P = np.where(allowed, np.exp(S - m[:, None]), 0.0)
+                l = P.sum(axis=1)
+                P = P / np.where(live, l, 1.0)[:, None]
+                dO = do[b, rr, h, :]
+                dV[b, :, kvh, :] += P.T @ dO
+                dP = dO @ Vb.T
+                dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                dQ[b, rr, h, :] = scale * (dS @ Kb)
+                dK[b, :, kvh, :] += scale * (dS.T @ q[b, rr, h, :])
+    return dQ, dK, dV
