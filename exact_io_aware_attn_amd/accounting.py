@@ -5,6 +5,11 @@ Inference", "Why Decode is Memory-bound"): a score is a length-d dot product,
 about 2d FLOPs, and so is each row of P V, so every attended (query, key) pair
 costs 4d FLOPs; decode streams every cached key and value once.
 
+The backward pass by recomputation (FlashAttention explainer, §4 재계산)
+rebuilds S once and forms dV, dP, dQ and dK: five length-d products, 10d FLOPs
+per attended pair. Its compulsory HBM traffic reads Q, K, V, O, dO and the LSE
+once and writes dQ, dK and dV once.
+
 Only pairs that are actually attended count (causal: the lower triangle;
 block-sparse: live blocks only). Softmax work and the key-norm pre-pass are
 excluded from the FLOP count.
@@ -60,6 +65,16 @@ def prefill_io_bytes(B, Hq, Hkv, Nq, Nk, d, elem_bytes=2, lse=True):
     return int(b)
 
 
+def backward_flops(B, Hq, d, pairs_per_head):
+    """10 d FLOPs per attended pair (S recomputed, dV, dP, dQ, dK), all heads."""
+    return 10 * int(d) * int(pairs_per_head) * int(B) * int(Hq)
+
+
+def backward_io_bytes(B, Hq, Hkv, Nq, Nk, d, elem_bytes=2):
+    """Read Q, O, dO, K, V and the LSE once; write dQ, dK, dV once."""
+    return int(elem_bytes * d * (B * Nq * Hq * 4 + B * Nk * Hkv * 4) + 4 * B * Hq * Nq)
+
+
 def workload_work(w, block_mask=None, seqlens=None):
     """(flops, bytes) of one call of a named workload."""
     eb = 2 if w.dtype == "bf16" else 4
@@ -67,5 +82,8 @@ def workload_work(w, block_mask=None, seqlens=None):
         return decode_flops(seqlens, w.Hq, w.d), decode_kv_bytes(seqlens, w.Hkv, w.d, eb)
     pairs = attended_pairs(w.Nq, w.Nk, causal=w.causal, block_mask=block_mask,
                            block_q=w.block or None, block_k=w.block or None)
+    if w.kind == "backward":
+        return (backward_flops(w.B, w.Hq, w.d, pairs),
+                backward_io_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, eb))
     return (prefill_flops(w.B, w.Hq, w.d, pairs),
             prefill_io_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, eb))

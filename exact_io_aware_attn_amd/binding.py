@@ -22,7 +22,8 @@ MIATTN_MASK_NONE, MIATTN_MASK_CAUSAL, MIATTN_MASK_BLOCK = 0, 1, 2
 SOFTMAX_MODES = {"online": 0, "fixed_max": 1, "fixed_max_centered": 2}
 
 _EXPORTS = ("attn_fwd", "attn_fwd_workspace_bytes", "attn_decode",
-            "attn_decode_workspace_bytes", "attn_status_str")
+            "attn_decode_workspace_bytes", "attn_bwd", "attn_bwd_workspace_bytes",
+            "attn_status_str")
 
 
 class MiattnError(RuntimeError):
@@ -59,6 +60,11 @@ def library():
     lib.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I,
                                 ctypes.POINTER(_Strides), P, Z, P]
     lib.attn_decode.restype = I
+    lib.attn_bwd_workspace_bytes.argtypes = [I, I, I]
+    lib.attn_bwd_workspace_bytes.restype = Z
+    lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I,
+                             ctypes.POINTER(_Strides), P, Z, P]
+    lib.attn_bwd.restype = I
     _lib = lib
     return lib
 
@@ -74,6 +80,10 @@ def attn_fwd_workspace_bytes(B, Hkv, Nq, Nk, d, mask_kind, block_q, softmax_mode
 
 def attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d, kv_splits=0):
     return int(library().attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d, kv_splits))
+
+
+def attn_bwd_workspace_bytes(B, Hq, Nq):
+    return int(library().attn_bwd_workspace_bytes(B, Hq, Nq))
 
 
 def _dtype_code(t):
@@ -229,3 +239,50 @@ def prepare_decode(q, k_cache, v_cache, seqlens, *, scale=None, kv_splits=0, ret
     args, o, lse, keep = _decode_setup(q, k_cache, v_cache, seqlens, scale, kv_splits,
                                        return_lse, out, lse_out, workspace)
     return PreparedCall(library().attn_decode, args, "attn_decode", keep), o, lse
+
+
+def _bwd_setup(q, k, v, o, lse, dout, causal, scale, dq, dk, dv, workspace):
+    _check_gpu(q, k, v, o, lse, dout)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or o.shape != q.shape \
+            or dout.shape != q.shape:
+        raise ValueError("q, o, dout must be [B,Nq,Hq,d]; k and v [B,Nk,Hkv,d]")
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    if lse.shape != (B, Hq, Nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B,Hq,Nq]")
+    dev = q.device
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lse = lse.contiguous()
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_gpu(dq, dk, dv)
+    need = attn_bwd_workspace_bytes(B, Hq, Nq)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = (_Strides * 8)(*[_strides4(t) for t in (q, k, v, o, dout, dq, dk, dv)])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    mask_kind = MIATTN_MASK_CAUSAL if causal else MIATTN_MASK_NONE
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+            _ptr(dv), _dtype_code(q), B, Hq, Hkv, Nq, Nk, d, scale, mask_kind, st,
+            _ptr(workspace), ws_bytes, _stream(dev))
+    return args, (dq, dk, dv), (q, k, v, o, lse, dout, dq, dk, dv, workspace, st)
+
+
+def attn_bwd(q, k, v, o, lse, dout, *, causal=False, scale=None, dq=None, dk=None, dv=None,
+             workspace=None):
+    """Gradients of attention with respect to q, k, v (bf16 GPU tensors) for the
+    upstream gradient dout, given the forward's o and lse [B,Hq,Nq] (float32).
+    Returns (dq, dk, dv)."""
+    args, grads, _ = _bwd_setup(q, k, v, o, lse, dout, causal, scale, dq, dk, dv, workspace)
+    rc = library().attn_bwd(*args)
+    if rc != 0:
+        raise MiattnError(rc, "attn_bwd")
+    return grads
+
+
+def prepare_bwd(q, k, v, o, lse, dout, *, causal=False, scale=None, dq=None, dk=None, dv=None,
+                workspace=None):
+    """attn_bwd as a PreparedCall: returns (call, (dq, dk, dv))."""
+    args, grads, keep = _bwd_setup(q, k, v, o, lse, dout, causal, scale, dq, dk, dv, workspace)
+    return PreparedCall(library().attn_bwd, args, "attn_bwd", keep), grads

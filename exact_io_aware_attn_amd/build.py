@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmiattn.so")
-SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "kstats.hip", "decode.hip", "segments.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "kstats.hip", "decode.hip", "segments.hip", "bwd_bf16.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

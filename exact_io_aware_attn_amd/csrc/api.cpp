@@ -264,4 +264,73 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
   return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;
 }
 
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq) {
+  if (B < 0 || Hq <= 0 || Nq < 0) return 0;
+  const size_t npad = (size_t)(Nq + 63) / 64 * 64;
+  return align_up(2 * (size_t)B * Hq * npad * sizeof(float));
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int dtype, int B, int Hq,
+             int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
+             const miattn_strides* strides, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  if (dtype != MIATTN_BF16) return MIATTN_ERR_UNSUPPORTED;
+  if (B < 0 || Nq < 0 || Nk < 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return MIATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return MIATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return MIATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return MIATTN_ERR_ARG;
+  if (mask_kind < 0 || mask_kind > (MIATTN_MASK_CAUSAL | MIATTN_MASK_BLOCK)) return MIATTN_ERR_ARG;
+  if (mask_kind & MIATTN_MASK_BLOCK) return MIATTN_ERR_UNSUPPORTED;
+  if (B == 0 || (Nq == 0 && Nk == 0)) return MIATTN_OK;
+  if (Nq > 0 && (q == nullptr || o == nullptr || dout == nullptr || lse == nullptr || dq == nullptr))
+    return MIATTN_ERR_NULL;
+  if (Nk > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+    return MIATTN_ERR_NULL;
+
+  miattn_strides sq{(int64_t)Nq * Hq * d, (int64_t)Hq * d, d};
+  miattn_strides sk{(int64_t)Nk * Hkv * d, (int64_t)Hkv * d, d};
+  miattn_strides st[8] = {sq, sk, sk, sq, sq, sq, sk, sk};  // q k v o dout dq dk dv
+  if (strides != nullptr)
+    for (int i = 0; i < 8; ++i) st[i] = strides[i];
+  for (int i = 0; i < 8; ++i) {
+    if (!strides_ok(st[i], 8)) return MIATTN_ERR_UNSUPPORTED;
+    if (st[i].s < d) return MIATTN_ERR_UNSUPPORTED;  // rows must not overlap
+  }
+  const void* ptrs[8] = {q, k, v, o, dout, dq, dk, dv};
+  for (int i = 0; i < 8; ++i)
+    if (ptrs[i] != nullptr && !aligned16(ptrs[i])) return MIATTN_ERR_UNSUPPORTED;
+  // streamed tiles are addressed with 32-bit byte offsets within one
+  // (batch, head) of Q, dO, K and V
+  const int64_t lim = (int64_t)1 << 31;
+  if ((int64_t)Nq * st[0].s * 2 >= lim || (int64_t)Nq * st[4].s * 2 >= lim ||
+      (int64_t)Nk * st[1].s * 2 >= lim || (int64_t)Nk * st[2].s * 2 >= lim)
+    return MIATTN_ERR_UNSUPPORTED;
+  const size_t need = attn_bwd_workspace_bytes(B, Hq, Nq);
+  if (need >= (size_t)lim) return MIATTN_ERR_UNSUPPORTED;  // statistics offsets are 32-bit
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MIATTN_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return MIATTN_ERR_UNSUPPORTED;
+
+  miattn::BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.q_sb = st[0].b; p.q_ss = st[0].s; p.q_sh = st[0].h;
+  p.k_sb = st[1].b; p.k_ss = st[1].s; p.k_sh = st[1].h;
+  p.v_sb = st[2].b; p.v_ss = st[2].s; p.v_sh = st[2].h;
+  p.o_sb = st[3].b; p.o_ss = st[3].s; p.o_sh = st[3].h;
+  p.do_sb = st[4].b; p.do_ss = st[4].s; p.do_sh = st[4].h;
+  p.dq_sb = st[5].b; p.dq_ss = st[5].s; p.dq_sh = st[5].h;
+  p.dk_sb = st[6].b; p.dk_ss = st[6].s; p.dk_sh = st[6].h;
+  p.dv_sb = st[7].b; p.dv_ss = st[7].s; p.dv_sh = st[7].h;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.causal_off = Nk - Nq;
+  p.npad = (Nq + 63) / 64 * 64;
+  p.stats = (float*)workspace;
+  hipError_t e = miattn::launch_bwd_bf16(p, d, (mask_kind & MIATTN_MASK_CAUSAL) != 0,
+                                         (hipStream_t)stream);
+  return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;
+}
+
 }  // extern "C"

@@ -1,0 +1,474 @@
+// Backward pass of exact attention by recomputation, bf16 in and out, fp32
+// accumulation, gfx950 MFMA (v_mfma_f32_32x32x16_bf16).
+//
+// FlashAttention explainer (base.kaita.kr), §4 재계산: the forward pass keeps
+// only O and the row statistics; the backward pass rebuilds S and P tile by
+// tile from Q, K, V in on-chip memory instead of reading an N x N matrix. Per
+// (query i, key j) pair, with P_ij = exp(scale * q_i . k_j - LSE_i):
+//   dV_j += P_ij dO_i,   dP_ij = dO_i . v_j,   dS_ij = P_ij (dP_ij - D_i),
+//   dQ_i += scale dS_ij k_j,   dK_j += scale dS_ij q_i,
+// where D_i = dO_i . O_i equals sum_j P_ij dP_ij (the row term of the softmax
+// Jacobian). Three kernels, no atomics (outputs are bitwise repeatable):
+//  * bwd_prep_kernel: D_i and LSE_i * log2(e) per row into the workspace.
+//  * bwd_dkdv_kernel: keys stationary (32 per wave, 128 per workgroup), K and
+//    V in registers; Q and dO tiles of 64 rows stream through LDS for every
+//    query head of the group, so dK and dV sum the group in registers.
+//  * bwd_dq_kernel: queries stationary (32 per wave), Q and dO in registers;
+//    K and V tiles of 64 keys stream through LDS.
+// Both main kernels stage tiles HBM -> LDS with the LDS-DMA loads the forward
+// kernel uses (rows past the end read as zeros), double-buffered with one
+// barrier per tile, and skip tiles the causal rule hides entirely.
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace miattn {
+
+namespace {
+
+constexpr int BT = 64;  // rows of a streamed tile (queries or keys)
+constexpr int NW = 4;   // waves per workgroup, 32 stationary rows each
+
+// A-operand fragment of a [BT][D] LDS tile read as rows: lane (i, h) gets row
+// 32*blk + i, elements 16*ks + 8*h .. +8 (TR: the tile uses vswz, else kswz).
+template <int D, bool TR>
+__device__ __forceinline__ bf16x8 row_frag(const __bf16* t, int blk, int ks, int qc, int h) {
+  const int row = 32 * blk + qc;
+  const int ch = 2 * ks + h;
+  const int slot = TR ? vswz<D>(row, ch) : kswz<D>(row, ch);
+  return *(const bf16x8*)(t + row * D + slot * 8);
+}
+
+// A-operand fragment of the transposed tile for the 16-row step u and the
+// 32-column block mb: lane (i, h') gets columns 32*mb + i of rows
+// 16u + 8*(e/4) + 4h' + e%4, e = 0..7 -- the row order in which the 32x32
+// accumulator holds them, so the accumulator serves as the B operand as is.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const __bf16* t, int u, int mb, int tr_row, int tr_ch,
+                                          int tr_half) {
+  const int ch = 4 * mb + tr_ch;
+  const int r0 = 16 * u + tr_row, r1 = 16 * u + 8 + tr_row;
+  const s16x4 lo = lds_tr16(t + r0 * D + vswz<D>(r0, ch) * 8 + tr_half);
+  const s16x4 hi = lds_tr16(t + r1 * D + vswz<D>(r1, ch) * 8 + tr_half);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// bytes covering rows [0, n) of a [rows, stride] view with D elements per row
+template <int D>
+__device__ __forceinline__ uint32_t span(int n, int64_t stride) {
+  return n > 0 ? (uint32_t)(((int64_t)(n - 1) * stride + D) * 2) : 0u;
+}
+
+// ---- D_i = dO_i . O_i (fp32) and LSE_i * log2(e), per (batch, head, row);
+// rows Nq .. npad-1 get D = 0 and +inf (their weights exp2(s - inf) are 0).
+// D/8 lanes per row, 16 bytes each.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_prep_kernel(const BwdParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const int64_t total = (int64_t)p.B * p.Hq * p.npad;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int ch = threadIdx.x % LPR;
+  if (row >= total) return;  // whole groups of LPR lanes leave together
+  const int i = (int)(row % p.npad);
+  const int64_t bh = row / p.npad;
+  const int hq = (int)(bh % p.Hq);
+  const int b = (int)(bh / p.Hq);
+  float acc = 0.f;
+  if (i < p.Nq) {
+    const bf16x8 o = *(const bf16x8*)((const __bf16*)p.o + b * p.o_sb + (int64_t)i * p.o_ss +
+                                      hq * p.o_sh + 8 * ch);
+    const bf16x8 g = *(const bf16x8*)((const __bf16*)p.dout + b * p.do_sb +
+                                      (int64_t)i * p.do_ss + hq * p.do_sh + 8 * ch);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(bf2f(o[e]), bf2f(g[e]), acc);
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += shfl_xor(acc, m);
+  if (ch == 0) {
+    p.stats[row] = i < p.Nq ? p.lse[bh * p.Nq + i] * kLog2e : __builtin_inff();
+    p.stats[total + row] = acc;
+  }
+}
+
+// ---- dK and dV. Workgroup: 128 keys of one (batch, KV head); wave w holds
+// keys 32w .. 32w+31 as B operands (lane (c, h): key c, elements 16t + 8h).
+// S[q][key] = Q K^T and dP[q][key] = dO V^T come out with lane (c, h)
+// holding key c for the 16 query rows 8*(r/4) + 4h + r%4 of a 32-row block;
+// P and dS in that layout are the B operands of dV^T += dO^T P and
+// dK^T += Q^T dS, whose A operands are transposed reads of the dO and Q tiles.
+// d = 128 holds K, V and both accumulators (192 registers) plus the tile's
+// S and dP: one wave per SIMD, so nothing spills.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(const BwdParams p) {
+  constexpr int CH = D / 8;
+  constexpr int KSTEPS = D / 16;
+  constexpr int MB = D / 32;
+  constexpr int RPI = 1024 / (D * 2);  // tile rows per 1 KiB load instruction
+  constexpr int NIW = BT / RPI / NW;   // load instructions per wave per tile and tensor
+
+  __shared__ __attribute__((aligned(16))) __bf16 sQ[2][BT * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sG[2][BT * D];    // dO
+  __shared__ __attribute__((aligned(16))) float sSt[2][2 * BT];   // lse2 then dsum
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int qc = lane & 31;
+  const int h = lane >> 5;
+
+  const int nbh = p.B * p.Hkv;
+  const int bh = blockIdx.x % nbh;
+  const int kt = blockIdx.x / nbh;  // key tiles in order: causal ones with most queries first
+  const int b = bh / p.Hkv;
+  const int hkv = bh % p.Hkv;
+  const int G = p.Hq / p.Hkv;
+  const int k0w = kt * 128 + 32 * wave;  // first key of this wave
+  const int key = k0w + qc;
+  const bool key_ok = key < p.Nk;
+
+  // stationary K and V fragments
+  bf16x8 kf[KSTEPS], vf[KSTEPS];
+  {
+    const __bf16* kp = (const __bf16*)p.k + b * p.k_sb + (int64_t)key * p.k_ss + hkv * p.k_sh + 8 * h;
+    const __bf16* vp = (const __bf16*)p.v + b * p.v_sb + (int64_t)key * p.v_ss + hkv * p.v_sh + 8 * h;
+    const bf16x8 z = {};
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      kf[t] = key_ok ? *(const bf16x8*)(kp + 16 * t) : z;
+      vf[t] = key_ok ? *(const bf16x8*)(vp + 16 * t) : z;
+    }
+  }
+
+  // queries that can see the workgroup's keys: q >= key - causal_off
+  int qb0 = 0;
+  if constexpr (CAUSAL) qb0 = max(0, kt * 128 - p.causal_off) / BT * BT;
+  const int n_qt = p.Nq > qb0 ? (p.Nq - qb0 + BT - 1) / BT : 0;
+  const int n_steps = G * n_qt;  // step s: query head hkv*G + s / n_qt, tile s % n_qt
+
+  // ---- staging: instruction j of this wave fills tile rows
+  // (wave*NIW + j)*RPI + lane/CH, LDS slot lane%CH holding chunk vswz(r, slot)
+  const int dma_row0 = wave * NIW * RPI + lane / CH;
+  const int dma_slot = lane % CH;
+  uint32_t qo[NIW], go[NIW];
+#pragma unroll
+  for (int j = 0; j < NIW; ++j) {
+    const int r = dma_row0 + j * RPI;
+    qo[j] = (uint32_t)(r * p.q_ss + vswz<D>(r, dma_slot) * 8) * 2u;
+    go[j] = (uint32_t)(r * p.do_ss + vswz<D>(r, dma_slot) * 8) * 2u;
+  }
+  const int64_t nstat = (int64_t)p.B * p.Hq * p.npad;
+  const DmaRsrc rst = dma_rsrc(p.stats, (uint32_t)(2 * nstat * 4));
+  auto issue = [&](int st, int buf) {
+    const int g = st / n_qt;
+    const int r0 = qb0 + (st - g * n_qt) * BT;
+    const int hq = hkv * G + g;
+    const int nvalid = min(BT, p.Nq - r0);
+    const __bf16* qb = (const __bf16*)p.q + b * p.q_sb + (int64_t)r0 * p.q_ss + hq * p.q_sh;
+    const __bf16* gb = (const __bf16*)p.dout + b * p.do_sb + (int64_t)r0 * p.do_ss + hq * p.do_sh;
+    const DmaRsrc rq = dma_rsrc(qb, span<D>(nvalid, p.q_ss));
+    const DmaRsrc rg = dma_rsrc(gb, span<D>(nvalid, p.do_ss));
+#pragma unroll
+    for (int j = 0; j < NIW; ++j) {
+      const int lds_row = (wave * NIW + j) * RPI;
+      buf_load_lds16(rq, sQ[buf] + lds_row * D, qo[j]);
+      buf_load_lds16(rg, sG[buf] + lds_row * D, go[j]);
+    }
+    // statistics of the tile's 64 rows (always inside the padded rows):
+    // lanes 0-15 the lse2 row, lanes 16-31 the dsum row, 16 bytes each
+    if (wave == 0 && lane < 32) {
+      const int64_t srow = ((int64_t)b * p.Hq + hq) * p.npad + r0;
+      const uint32_t off = (uint32_t)((srow + (lane >= 16 ? nstat : 0)) * 4 + 16 * (lane & 15));
+      buf_load_lds16(rst, sSt[buf], off);
+    }
+  };
+
+  f32x16 dkacc[MB], dvacc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dkacc[mb][r] = dvacc[mb][r] = 0.f;
+  const float c = p.scale_log2;
+  const int tr_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_ch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_half = 4 * (lane & 1);
+
+  auto body = [&](int st, int buf) {
+    const int g = st / n_qt;
+    const int r0 = qb0 + (st - g * n_qt) * BT;
+    const __bf16* sq = sQ[buf];
+    const __bf16* sg = sG[buf];
+    const float* ss = sSt[buf];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qs = r0 + 32 * qb;  // first query row of the block
+      // 0: no pair visible, 1: all visible, 2: apply the causal rule
+      int state = 1;
+      if (qs >= p.Nq) state = 0;
+      else if (CAUSAL) {
+        if (qs + 31 + p.causal_off < k0w) state = 0;
+        else if (qs + p.causal_off < k0w + 31) state = 2;
+      }
+      if (state == 0) continue;
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t) {
+        s = mfma32(row_frag<D, true>(sq, qb, t, qc, h), kf[t], s);
+        dp = mfma32(row_frag<D, true>(sg, qb, t, qc, h), vf[t], dp);
+      }
+      // P = exp2(c s - lse2) and dS = P (dP - D) per row 8j + 4h + i
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 l4 = *(const f32x4*)(ss + 32 * qb + 8 * j + 4 * h);
+        const f32x4 d4 = *(const f32x4*)(ss + BT + 32 * qb + 8 * j + 4 * h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * j + i;
+          float pr = ex2(__builtin_fmaf(s[r], c, -l4[i]));
+          if (CAUSAL && state == 2) {
+            const int q = qs + 8 * j + 4 * h + i;
+            pr = key <= q + p.causal_off ? pr : 0.f;
+          }
+          s[r] = pr;
+          dp[r] = pr * (dp[r] - d4[i]);
+        }
+      }
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const int u = 2 * qb + uu;
+        const int o8 = 8 * uu;
+        const bf16x8 pf = cvt8(s[o8 + 0], s[o8 + 1], s[o8 + 2], s[o8 + 3], s[o8 + 4], s[o8 + 5],
+                               s[o8 + 6], s[o8 + 7]);
+        const bf16x8 df = cvt8(dp[o8 + 0], dp[o8 + 1], dp[o8 + 2], dp[o8 + 3], dp[o8 + 4],
+                               dp[o8 + 5], dp[o8 + 6], dp[o8 + 7]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          dvacc[mb] = mfma32(tr_frag<D>(sg, u, mb, tr_row, tr_ch, tr_half), pf, dvacc[mb]);
+          dkacc[mb] = mfma32(tr_frag<D>(sq, u, mb, tr_row, tr_ch, tr_half), df, dkacc[mb]);
+        }
+      }
+    }
+  };
+
+  if (n_steps > 0) issue(0, 0);
+  wait_all_loads();
+  __syncthreads();
+  for (int st = 0; st < n_steps; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < n_steps) issue(st + 1, buf ^ 1);
+    body(st, buf);
+    wait_all_loads();
+    __syncthreads();  // buffer buf free; step st+1 landed in buf^1
+  }
+
+  // ---- epilogue: dK = scale * acc, dV = acc; lane (c, h) holds dims
+  // 32mb + 8jj + 4h .. +3 of key c
+  if (key_ok) {
+    __bf16* dkp = (__bf16*)p.dk + b * p.dk_sb + (int64_t)key * p.dk_ss + hkv * p.dk_sh;
+    __bf16* dvp = (__bf16*)p.dv + b * p.dv_sb + (int64_t)key * p.dv_ss + hkv * p.dv_sh;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x16& a = dkacc[mb];
+        const f32x16& v = dvacc[mb];
+        *(bf16x4*)(dkp + 32 * mb + 8 * jj + 4 * h) =
+            cvt4(a[4 * jj] * p.scale, a[4 * jj + 1] * p.scale, a[4 * jj + 2] * p.scale,
+                 a[4 * jj + 3] * p.scale);
+        *(bf16x4*)(dvp + 32 * mb + 8 * jj + 4 * h) =
+            cvt4(v[4 * jj], v[4 * jj + 1], v[4 * jj + 2], v[4 * jj + 3]);
+      }
+  }
+}
+
+// ---- dQ. Workgroup: 128 query rows of one (batch, query head); wave w holds
+// rows 32w .. 32w+31 as B operands (lane (c, h): row c). S^T = K Q^T and
+// dP^T = V dO^T come out with lane (c, h) holding query c for the 16 keys
+// 8*(r/4) + 4h + r%4 of a 32-key block; dS^T in that layout is the B operand
+// of dQ^T += K^T dS^T, whose A operand is a transposed read of the K tile.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
+  constexpr int CH = D / 8;
+  constexpr int KSTEPS = D / 16;
+  constexpr int MB = D / 32;
+  constexpr int RPI = 1024 / (D * 2);
+  constexpr int NIW = BT / RPI / NW;
+
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2][BT * D];  // vswz (read both ways)
+  __shared__ __attribute__((aligned(16))) __bf16 sV[2][BT * D];  // kswz (read as rows)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int qc = lane & 31;
+  const int h = lane >> 5;
+
+  const int n_qt = (p.Nq + 127) / 128;
+  const int hq = blockIdx.x % p.Hq;
+  const int t2 = blockIdx.x / p.Hq;
+  const int b = t2 % p.B;
+  const int rank = t2 / p.B;
+  const int qt = CAUSAL ? n_qt - 1 - rank : rank;  // causal: longest rows first
+  const int hkv = hq / (p.Hq / p.Hkv);
+  const int q0 = qt * 128 + 32 * wave;
+  const int qrow = q0 + qc;
+  const bool row_ok = qrow < p.Nq;
+  const int wave_last = min(q0 + 31, p.Nq - 1);
+
+  bf16x8 qf[KSTEPS], gf[KSTEPS];
+  {
+    const __bf16* qp = (const __bf16*)p.q + b * p.q_sb + (int64_t)qrow * p.q_ss + hq * p.q_sh + 8 * h;
+    const __bf16* gp =
+        (const __bf16*)p.dout + b * p.do_sb + (int64_t)qrow * p.do_ss + hq * p.do_sh + 8 * h;
+    const bf16x8 z = {};
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      qf[t] = row_ok ? *(const bf16x8*)(qp + 16 * t) : z;
+      gf[t] = row_ok ? *(const bf16x8*)(gp + 16 * t) : z;
+    }
+  }
+  const int64_t nstat = (int64_t)p.B * p.Hq * p.npad;
+  const int64_t srow = ((int64_t)b * p.Hq + hq) * p.npad;
+  const float lse2 = row_ok ? p.stats[srow + qrow] : __builtin_inff();
+  const float dsum = row_ok ? p.stats[nstat + srow + qrow] : 0.f;
+
+  int kv_end = p.Nk;
+  if constexpr (CAUSAL)
+    kv_end = min(p.Nk, max(0, min(qt * 128 + 127, p.Nq - 1) + p.causal_off + 1));
+  const int n_tiles = (kv_end + BT - 1) / BT;
+
+  const __bf16* kg = (const __bf16*)p.k + b * p.k_sb + hkv * p.k_sh;
+  const __bf16* vg = (const __bf16*)p.v + b * p.v_sb + hkv * p.v_sh;
+  const int dma_row0 = wave * NIW * RPI + lane / CH;
+  const int dma_slot = lane % CH;
+  uint32_t ko[NIW], vo[NIW];
+#pragma unroll
+  for (int j = 0; j < NIW; ++j) {
+    const int r = dma_row0 + j * RPI;
+    ko[j] = (uint32_t)(r * p.k_ss + vswz<D>(r, dma_slot) * 8) * 2u;
+    vo[j] = (uint32_t)(r * p.v_ss + kswz<D>(r, dma_slot) * 8) * 2u;
+  }
+  auto issue = [&](int t, int buf) {
+    const int r0 = t * BT;
+    const int nvalid = min(BT, kv_end - r0);
+    const DmaRsrc rk = dma_rsrc(kg + (int64_t)r0 * p.k_ss, span<D>(nvalid, p.k_ss));
+    const DmaRsrc rv = dma_rsrc(vg + (int64_t)r0 * p.v_ss, span<D>(nvalid, p.v_ss));
+#pragma unroll
+    for (int j = 0; j < NIW; ++j) {
+      const int lds_row = (wave * NIW + j) * RPI;
+      buf_load_lds16(rk, sK[buf] + lds_row * D, ko[j]);
+      buf_load_lds16(rv, sV[buf] + lds_row * D, vo[j]);
+    }
+  };
+
+  f32x16 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+  const float c = p.scale_log2;
+  const int tr_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_ch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_half = 4 * (lane & 1);
+
+  auto body = [&](int t, int buf) {
+    const int k0 = t * BT;
+    int state = 1;  // 0: nothing visible, 1: all visible, 2: apply the rules
+    if (q0 >= p.Nq) state = 0;
+    else {
+      if (CAUSAL) {
+        if (k0 > wave_last + p.causal_off) state = 0;
+        else if (k0 + BT - 1 > q0 + p.causal_off) state = 2;
+      }
+      if (state == 1 && k0 + BT > p.Nk) state = 2;
+    }
+    if (state == 0) return;
+    const __bf16* sk = sK[buf];
+    const __bf16* sv = sV[buf];
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        s[kb] = mfma32(row_frag<D, true>(sk, kb, ks, qc, h), qf[ks], s[kb]);
+        dp[kb] = mfma32(row_frag<D, false>(sv, kb, ks, qc, h), gf[ks], dp[kb]);
+      }
+    }
+    // dS^T = P^T (dP^T - D) in place of dP^T
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = ex2(__builtin_fmaf(s[kb][r], c, -lse2));
+        if (state == 2) {
+          const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          bool ok = kk < p.Nk;
+          if (CAUSAL) ok = ok && kk <= qrow + p.causal_off;
+          pr = ok ? pr : 0.f;
+        }
+        dp[kb][r] = pr * (dp[kb][r] - dsum);
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f32x16& sb = dp[u >> 1];
+      const int o8 = 8 * (u & 1);
+      const bf16x8 df = cvt8(sb[o8 + 0], sb[o8 + 1], sb[o8 + 2], sb[o8 + 3], sb[o8 + 4], sb[o8 + 5],
+                             sb[o8 + 6], sb[o8 + 7]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = mfma32(tr_frag<D>(sk, u, mb, tr_row, tr_ch, tr_half), df, acc[mb]);
+    }
+  };
+
+  if (n_tiles > 0) issue(0, 0);
+  wait_all_loads();
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) issue(t + 1, buf ^ 1);
+    body(t, buf);
+    wait_all_loads();
+    __syncthreads();
+  }
+
+  if (row_ok) {
+    __bf16* op = (__bf16*)p.dq + b * p.dq_sb + (int64_t)qrow * p.dq_ss + hq * p.dq_sh;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x16& a = acc[mb];
+        *(bf16x4*)(op + 32 * mb + 8 * jj + 4 * h) =
+            cvt4(a[4 * jj] * p.scale, a[4 * jj + 1] * p.scale, a[4 * jj + 2] * p.scale,
+                 a[4 * jj + 3] * p.scale);
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const BwdParams& p, hipStream_t s) {
+  const int64_t rows = (int64_t)p.B * p.Hq * p.npad;
+  if (rows > 0) {
+    constexpr int RPB = 256 / (D / 8);
+    hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                       s, p);
+  }
+  const int64_t nkw = (int64_t)((p.Nk + 127) / 128) * p.B * p.Hkv;
+  if (nkw > 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)nkw), dim3(64 * NW), 0, s, p);
+  const int64_t nqw = (int64_t)((p.Nq + 127) / 128) * p.B * p.Hq;
+  if (nqw > 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)nqw), dim3(64 * NW), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t s) {
+  if (d == 64) return causal ? launch<64, true>(p, s) : launch<64, false>(p, s);
+  return causal ? launch<128, true>(p, s) : launch<128, false>(p, s);
+}
+
+}  // namespace miattn

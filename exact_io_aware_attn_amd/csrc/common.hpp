@@ -140,6 +140,22 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// LDS swizzles of [rows][D] bf16 tiles on 16-byte chunks (row r, logical
+// chunk ch -> slot), chosen so the MFMA-side reads hit distinct banks: kswz
+// for tiles read as rows (16 rows x one chunk per 16 lanes), vswz for tiles
+// read by the transpose load (4 rows x 2 chunks per 16 lanes). Both are
+// involutions.
+template <int D>
+__device__ __forceinline__ int kswz(int r, int ch) {
+  if constexpr (D == 128) return ch ^ (r & 15);
+  else return ch ^ ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int r, int ch) {
+  if constexpr (D == 128) return ch ^ ((r & 3) << 2);
+  else return ch ^ (((r >> 1) & 1) << 2);
+}
+
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }

@@ -68,20 +68,6 @@ namespace {
 constexpr int BK = 64;   // keys per tile
 constexpr float kBlkSumMax = 4096.f;  // lazy rescale: a lane's 16-value block sum above this
 
-// LDS swizzles on 16-byte chunks, chosen so the MFMA-side reads hit distinct
-// banks: K is read 16 rows x one chunk per 16 lanes; V is read by the
-// transpose load 4 rows x 2 chunks per 16 lanes.
-template <int D>
-__device__ __forceinline__ int kswz(int r, int ch) {
-  if constexpr (D == 128) return ch ^ (r & 15);
-  else return ch ^ ((r >> 1) & 7);
-}
-template <int D>
-__device__ __forceinline__ int vswz(int r, int ch) {
-  if constexpr (D == 128) return ch ^ ((r & 3) << 2);
-  else return ch ^ (((r >> 1) & 1) << 2);
-}
-
 // Hardware workgroup id -> (logical tile X, member g of the head group).
 // Groups of 8*G consecutive ids keep the G query heads of one KV head on one
 // XCD (ids are dealt round-robin over the 8 XCDs).

@@ -74,6 +74,34 @@ struct DecodeParams {
   float* part_lse;   // [n_splits + B][Hq]
 };
 
+// Backward pass (bf16). The statistics live in the caller's workspace, one
+// row of npad floats per (batch, query head), lse2 rows first, then dsum rows.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;   // [B][Hq][Nq], natural log (the forward's output)
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t do_sb, do_ss, do_sh;
+  int64_t dq_sb, dq_ss, dq_sh;
+  int64_t dk_sb, dk_ss, dk_sh;
+  int64_t dv_sb, dv_ss, dv_sh;
+  int B, Hq, Hkv, Nq, Nk;
+  float scale;        // softmax scale on q . k
+  float scale_log2;   // scale * log2(e)
+  int causal_off;     // Nk - Nq
+  int npad;           // Nq rounded up to 64
+  float* stats;       // [2][B*Hq][npad]: lse * log2(e) (+inf past Nq), rowsum(dO * O) (0 past Nq)
+};
+
 constexpr int kMaxSplits = 4096;
 int decode_waves_per_group(int Hkv);
 
@@ -84,6 +112,7 @@ hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, bool block,
 hipError_t launch_kstats(const KStatParams& p, int d, bool bf16, bool centred,
                          hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t s);
 
 inline int64_t align16(int64_t n) { return (n + 15) & ~(int64_t)15; }
 // workspace bytes of the segment table of an Nq-row mask with block_q rows per block

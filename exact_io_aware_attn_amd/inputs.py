@@ -5,8 +5,9 @@ key lengths, the frame block mask). It holds none of the attention arithmetic,
 so the oracle and the HIP path can both be fed from it.
 
 Recipe: a ``torch.Generator`` on the target device, seeded with the workload's
-seed; draw order is key lengths (decode only), then Q, K, V as float32 standard
-normals; bf16 workloads round those draws to bf16 (round to nearest even).
+seed; draw order is key lengths (decode only), then Q, K, V (then the upstream
+gradient dO for the backward pass) as float32 standard normals; bf16 workloads
+round those draws to bf16 (round to nearest even).
 """
 
 from dataclasses import dataclass, field
@@ -18,7 +19,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "prefill" or "decode"
+    kind: str                 # "prefill", "decode" or "backward"
     B: int
     Hq: int
     Hkv: int
@@ -60,6 +61,13 @@ WORKLOADS = {
     "gpt2-medium-causal": Workload("gpt2-medium-causal", "prefill", B=64, Hq=16, Hkv=16,
                                    Nq=1024, Nk=1024, d=64, dtype="bf16", causal=True,
                                    seed=6),
+    # backward pass (dQ, dK, dV from Q, K, V, O, LSE and dO) on the prefill shapes
+    "llama3-8b-gqa-causal-8k-bwd": Workload("llama3-8b-gqa-causal-8k-bwd", "backward", B=1,
+                                            Hq=32, Hkv=8, Nq=8192, Nk=8192, d=128,
+                                            dtype="bf16", causal=True, seed=7),
+    "gpt2-medium-causal-bwd": Workload("gpt2-medium-causal-bwd", "backward", B=64, Hq=16,
+                                       Hkv=16, Nq=1024, Nk=1024, d=64, dtype="bf16",
+                                       causal=True, seed=8),
     "video-frames-16x880": Workload("video-frames-16x880", "prefill", B=1, Hq=24,
                                     Hkv=24, Nq=14080, Nk=14080, d=128, dtype="bf16",
                                     seed=5, frames=16, frame_len=880, block=80,
@@ -92,6 +100,16 @@ def prefill_inputs(B, Hq, Hkv, Nq, Nk, d, dtype=torch.bfloat16, seed=0, device="
     k = _randn((B, Nk, Hkv, d), g, device, dtype)
     v = _randn((B, Nk, Hkv, d), g, device, dtype)
     return q, k, v
+
+
+def backward_inputs(B, Hq, Hkv, Nq, Nk, d, dtype=torch.bfloat16, seed=0, device="cpu"):
+    """Q, K, V as prefill_inputs draws them, then dO [B,Nq,Hq,d]."""
+    g = _gen(device, seed)
+    q = _randn((B, Nq, Hq, d), g, device, dtype)
+    k = _randn((B, Nk, Hkv, d), g, device, dtype)
+    v = _randn((B, Nk, Hkv, d), g, device, dtype)
+    do = _randn((B, Nq, Hq, d), g, device, dtype)
+    return q, k, v, do
 
 
 def decode_inputs(B, Hq, Hkv, max_len, d, dtype=torch.bfloat16, seed=0, len_lo=1,
@@ -128,7 +146,11 @@ def frame_block_mask(frames, frame_len, block, window=1, ref_frame=0):
 
 def workload_inputs(w: Workload, device="cpu"):
     """Inputs of a named workload: prefill -> dict(q, k, v, block_mask?),
-    decode -> dict(seqlens, q, k_cache, v_cache)."""
+    decode -> dict(seqlens, q, k_cache, v_cache), backward -> dict(q, k, v, dout)."""
+    if w.kind == "backward":
+        q, k, v, do = backward_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.torch_dtype,
+                                      w.seed, device)
+        return dict(q=q, k=k, v=v, dout=do)
     if w.kind == "prefill":
         q, k, v = prefill_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.torch_dtype,
                                  w.seed, device)

@@ -155,6 +155,43 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 const miattn_strides* cache_strides, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace attn_bwd needs: two fp32 rows of Nq rounded up
+ * to 64 per (batch, query head) -- the forward LSE in base-2 units and
+ * D_i = dO_i . O_i. Returns 0 for invalid sizes. */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
+
+/* Backward pass by recomputation ("플래시어텐션: 메모리를 아끼는 정확한 어텐션",
+ * §4 재계산): from Q, K, V, the forward output O, its per-row LSE and the
+ * upstream gradient dO, the gradients of O = softmax(scale * Q K^T + mask) V
+ * with respect to Q, K and V. S and P are rebuilt tile by tile from Q, K, V
+ * and the LSE; no N x N matrix is stored. With GQA the gradient of a KV head
+ * is the sum over the query heads that read it.
+ *
+ * q, o, dout  device, [B, Nq, Hq, d] bf16        (read)
+ * k, v        device, [B, Nk, Hkv, d] bf16       (read)
+ * lse         device, float [B, Hq, Nq]          (read: attn_fwd's LSE for
+ *             the same q, k, v and mask, natural log)
+ * dq          device, [B, Nq, Hq, d] bf16        (written)
+ * dk, dv      device, [B, Nk, Hkv, d] bf16       (written; keys no query
+ *             sees get 0)
+ * dtype       MIATTN_BF16 (bf16 MFMA inputs, fp32 accumulation; P and dS are
+ *             rounded to bf16 for the products that consume them)
+ * d           64 or 128
+ * scale       > 0 and finite, the forward's scale
+ * mask_kind   MIATTN_MASK_NONE or MIATTN_MASK_CAUSAL (same rule as attn_fwd);
+ *             BLOCK returns MIATTN_ERR_UNSUPPORTED
+ * strides     NULL (packed) or an array of 8: q, k, v, o, dout, dq, dk, dv
+ * workspace   device, at least attn_bwd_workspace_bytes(B, Hq, Nq) bytes,
+ *             owned by the caller, overwritten by the call
+ * stream      hipStream_t
+ * A query row with no visible key gets dQ = 0 and adds nothing to dK, dV.
+ * Outputs must not overlap the inputs. */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int dtype, int B, int Hq,
+             int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
+             const miattn_strides* strides, void* workspace, size_t workspace_bytes,
+             void* stream);
+
 /* Static description of a status code. */
 const char* attn_status_str(int status);
 

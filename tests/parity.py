@@ -4,6 +4,13 @@ Tolerances: bf16 inputs with fp32 accumulation -- O max-abs <= 1e-2 and
 relative Frobenius <= 5e-3 over the tensor, LSE max-abs <= 1e-3; fp32 inputs --
 O and LSE max-abs <= 1e-5. Rows with no visible key must be exactly O = 0 and
 LSE = -inf on both sides.
+
+Gradients (bf16 backward): per tensor, relative Frobenius error <= 1e-2 and
+max-abs error <= 2e-2 * max|reference|. Every product consumes bf16 operands
+(Q, K, V, dO as given, P and dS rounded, relative error <= 2^-9 each), D_i is
+formed from the bf16 output O, and each result is rounded to bf16 (2^-9):
+a handful of independent 2^-9 terms per element. Where the exact gradient is
+identically zero, max-abs <= 1e-4 (fp32 cancellation noise).
 """
 
 import numpy as np
@@ -41,6 +48,32 @@ def check(o_gpu, O_ref, lse_gpu=None, LSE_ref=None, dtype="bf16", where=""):
             le = float(np.abs(l[fin] - LSE_ref[fin]).max())
             assert le <= tol["lse_abs"], f"{where}: LSE max-abs {le:.3e} > {tol['lse_abs']}"
     return mx
+
+
+GRAD_TOL = dict(rel_fro=1e-2, rel_max=2e-2)
+GRAD_ZERO_ABS = 1e-4
+
+
+def check_grad(g_gpu, G_ref, where=""):
+    """Gradient tensor against the fp64 reference; returns (rel_fro, rel_max)."""
+    g = to64(g_gpu)
+    assert g.shape == G_ref.shape, (g.shape, G_ref.shape)
+    assert np.isfinite(g).all(), f"{where}: non-finite gradient"
+    if G_ref.size == 0:
+        return 0.0, 0.0
+    scale = float(np.abs(G_ref).max())
+    if scale == 0.0:
+        # an exactly-zero gradient (one visible key: P = 1 and dP - D cancels)
+        # comes out as fp32 cancellation noise between dP (MFMA sums) and D
+        # (the pre-pass's sums), each of size |dO| |v| ~ sqrt(d)
+        got = float(np.abs(g).max())
+        assert got <= GRAD_ZERO_ABS, f"{where}: zero gradient expected, max-abs {got:.3e}"
+        return 0.0, got
+    rel = float(np.linalg.norm(g - G_ref) / np.linalg.norm(G_ref))
+    rmax = float(np.abs(g - G_ref).max() / scale)
+    assert rel <= GRAD_TOL["rel_fro"], f"{where}: rel-Frobenius {rel:.3e} > {GRAD_TOL['rel_fro']}"
+    assert rmax <= GRAD_TOL["rel_max"], f"{where}: max-abs/max|ref| {rmax:.3e} > {GRAD_TOL['rel_max']}"
+    return rel, rmax
 
 
 def sample_rows(n, tile=128, extra=16, seed=0, boundaries=()):

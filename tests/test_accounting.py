@@ -54,3 +54,15 @@ def test_workload_figures():
     pairs = acc.attended_pairs(w.Nq, w.Nk, block_mask=bm, block_q=80, block_k=80)
     assert pairs == 46_464_000
     assert acc.workload_work(w, block_mask=bm)[0] == 46_464_000 * 24 * 512
+
+
+def test_backward_work_counts():
+    # 10 d FLOPs per attended pair: S recomputed, then dV, dP, dQ and dK, each a
+    # length-d product per pair, i.e. 2.5 times the forward's 4 d
+    w = WORKLOADS["llama3-8b-gqa-causal-8k-bwd"]
+    f, b = acc.workload_work(w)
+    pairs = 8192 * 8193 // 2
+    assert f == 10 * 128 * pairs * 32
+    assert f * 2 == 5 * acc.workload_work(WORKLOADS["llama3-8b-gqa-causal-8k"])[0]
+    # read Q, O, dO (queries) and K, V; write dQ, dK, dV; read the LSE
+    assert b == 2 * 128 * (8192 * 32 * 4 + 8192 * 8 * 4) + 4 * 32 * 8192

@@ -1,0 +1,133 @@
+"""attn_bwd on the GPU against the fp64 gradient oracle (element by element).
+
+The GPU side takes O and the LSE from attn_fwd on the same inputs, as a caller
+would; the oracle differentiates the definition from Q, K, V and dO alone.
+Small cases span several 128-row / 64-row tiles with ragged tails; full-size
+workloads are checked on sliced (batch, head group) pieces."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_attn_amd import attn_bwd, attn_fwd, prepare_bwd
+from exact_io_aware_attn_amd.inputs import WORKLOADS, backward_inputs, workload_inputs
+
+from parity import check_grad, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _gpu_grads(q, k, v, do, causal, scale=None):
+    q, k, v, do = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = attn_fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = attn_bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def _check(q, k, v, do, causal, where, scale=None):
+    d = q.shape[-1]
+    sc = 1 / math.sqrt(d) if scale is None else scale
+    dq, dk, dv = _gpu_grads(q, k, v, do, causal, scale)
+    ref = oracle.attention_backward(to64(q), to64(k), to64(v), to64(do), sc, causal=causal)
+    errs = [check_grad(g, r, f"{where} {n}") for g, r, n in zip((dq, dk, dv), ref, "QKV")]
+    print(where, " ".join(f"d{n} {e[0]:.2e}/{e[1]:.2e}" for n, e in zip("QKV", errs)))
+    return (dq, dk, dv), ref
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (2, 2)])
+@pytest.mark.parametrize("Nq,Nk", [(300, 333), (256, 256), (77, 200), (200, 77), (1, 130), (130, 1)])
+def test_bwd_shapes(d, causal, Hq, Hkv, Nq, Nk):
+    q, k, v, do = backward_inputs(2, Hq, Hkv, Nq, Nk, d, torch.bfloat16, seed=Nq * 5 + Nk + d)
+    (dq, _, _), _ = _check(q, k, v, do, causal, f"d={d} c={causal} H={Hq}/{Hkv} {Nq}x{Nk}")
+    if causal and Nq > Nk:
+        # rows Nq - Nk and below see no key: their gradient is exactly zero
+        assert (dq[:, : Nq - Nk].float() == 0).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_mqa_and_wide_groups(d):
+    q, k, v, do = backward_inputs(1, 8, 1, 190, 260, d, torch.bfloat16, seed=31 + d)
+    _check(q, k, v, do, True, f"MQA d={d}")
+
+
+def test_bwd_scale_argument():
+    q, k, v, do = backward_inputs(2, 4, 2, 160, 96, 64, torch.bfloat16, seed=5)
+    _check(q, k, v, do, False, "scale 0.3", scale=0.3)
+
+
+def test_bwd_strided_views():
+    # q, k, v as slices of one packed [B, N, 3, H, d] tensor; gradients written
+    # into slices of another
+    B, N, H, d = 2, 150, 4, 128
+    g = torch.Generator().manual_seed(17)
+    qkv = torch.randn(B, N, 3, H, d, generator=g).to(torch.bfloat16).to(DEV)
+    do = torch.randn(B, N, H, d, generator=g).to(torch.bfloat16).to(DEV)
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    o, lse = attn_fwd(q, k, v, causal=True)
+    grad = torch.zeros(B, N, 3, H, d, dtype=torch.bfloat16, device=DEV)
+    attn_bwd(q, k, v, o, lse, do, causal=True, dq=grad[:, :, 0], dk=grad[:, :, 1], dv=grad[:, :, 2])
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(to64(q), to64(k), to64(v), to64(do), 1 / math.sqrt(d), causal=True)
+    for i, n in enumerate("QKV"):
+        check_grad(grad[:, :, i], ref[i], f"strided d{n}")
+
+
+def test_bwd_empty_sides():
+    # no query rows: every key's gradient is zero; no keys: dQ is zero
+    q, k, v, do = (t.to(DEV) for t in backward_inputs(2, 4, 2, 0, 70, 64, torch.bfloat16, seed=1))
+    o = torch.empty_like(q)
+    lse = torch.empty(2, 4, 0, dtype=torch.float32, device=DEV)
+    dk = torch.full_like(k, 7.0)
+    dv = torch.full_like(v, 7.0)
+    attn_bwd(q, k, v, o, lse, do, causal=True, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert (dk.float() == 0).all() and (dv.float() == 0).all()
+    q, k, v, do = (t.to(DEV) for t in backward_inputs(2, 4, 2, 70, 0, 64, torch.bfloat16, seed=2))
+    o, lse = attn_fwd(q, k, v)
+    dq = torch.full_like(q, 7.0)
+    attn_bwd(q, k, v, o, lse, do, dq=dq)
+    torch.cuda.synchronize()
+    assert (dq.float() == 0).all()
+
+
+def test_bwd_bitwise_repeatable():
+    q, k, v, do = (t.to(DEV) for t in backward_inputs(1, 8, 2, 333, 333, 128, torch.bfloat16, seed=3))
+    o, lse = attn_fwd(q, k, v, causal=True)
+    call, grads = prepare_bwd(q, k, v, o, lse, do, causal=True)
+    call()
+    torch.cuda.synchronize()
+    first = [g.clone() for g in grads]
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    for a, b in zip(first, grads):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name,pieces", [
+    ("gpt2-medium-causal-bwd", [(0, 0), (63, 15), (17, 6)]),  # (batch, head)
+    ("llama3-8b-gqa-causal-8k-bwd", [(0, 3)]),                 # (batch, KV head)
+])
+def test_bwd_full_workload_sliced(name, pieces):
+    w = WORKLOADS[name]
+    ins = workload_inputs(w, device=DEV)
+    q, k, v, do = ins["q"], ins["k"], ins["v"], ins["dout"]
+    o, lse = attn_fwd(q, k, v, causal=w.causal)
+    dq, dk, dv = attn_bwd(q, k, v, o, lse, do, causal=w.causal)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    for b, hk in pieces:
+        hs = slice(hk * G, (hk + 1) * G)
+        ref = oracle.attention_backward(to64(q[b:b + 1, :, hs]), to64(k[b:b + 1, :, hk:hk + 1]),
+                                        to64(v[b:b + 1, :, hk:hk + 1]), to64(do[b:b + 1, :, hs]),
+                                        w.scale, causal=w.causal)
+        got = (dq[b:b + 1, :, hs], dk[b:b + 1, :, hk:hk + 1], dv[b:b + 1, :, hk:hk + 1])
+        errs = [check_grad(g_, r, f"{name} b={b} kv={hk} d{n}") for g_, r, n in zip(got, ref, "QKV")]
+        print(name, b, hk, " ".join(f"d{n} {e[0]:.2e}/{e[1]:.2e}" for n, e in zip("QKV", errs)))

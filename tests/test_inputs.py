@@ -51,5 +51,15 @@ def test_frame_mask_structure():
 def test_named_workloads():
     assert set(WORKLOADS) == {"tiny-f32", "gpt2-causal", "llama3-8b-gqa-causal-8k",
                               "gqa-decode-b64", "video-frames-16x880",
-                              "gpt2-medium-causal"}
+                              "gpt2-medium-causal", "llama3-8b-gqa-causal-8k-bwd",
+                              "gpt2-medium-causal-bwd"}
     assert WORKLOADS["llama3-8b-gqa-causal-8k"].scale == 1 / 128 ** 0.5
+
+
+def test_backward_inputs_extend_the_prefill_draws():
+    # same seed: Q, K, V are the prefill draws, dO comes after them
+    from exact_io_aware_attn_amd.inputs import backward_inputs, prefill_inputs
+    q, k, v = prefill_inputs(2, 4, 2, 33, 40, 64, torch.bfloat16, seed=9)
+    q2, k2, v2, do = backward_inputs(2, 4, 2, 33, 40, 64, torch.bfloat16, seed=9)
+    assert torch.equal(q, q2) and torch.equal(k, k2) and torch.equal(v, v2)
+    assert do.shape == q.shape and not torch.equal(do, q)
