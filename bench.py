@@ -22,7 +22,9 @@ Printed (one JSON line):
 --workload runs a single named workload instead (one call per step):
 gpt2-causal, gpt2-medium-causal, llama3-8b-gqa-causal-8k, gqa-decode-b64,
 video-frames-16x880 (online), video-frames-16x880-fixed,
-video-frames-16x880-centered, tiny-f32.
+video-frames-16x880-centered, tiny-f32, and the backward pass (attn_bwd, with
+O and the LSE from one attn_fwd call made before the timed steps; 10 d FLOPs
+per attended pair): llama3-8b-gqa-causal-8k-bwd, gpt2-medium-causal-bwd.
 """
 
 import argparse
@@ -113,6 +115,11 @@ class Part:
                 q, k, v, causal=w.causal, block_mask=self.bm,
                 block=(w.block, w.block) if self.bm is not None else None,
                 softmax=self.softmax, out=self.o, lse_out=self.lse, workspace=self.ws)
+        elif w.kind == "backward":
+            q, k, v, do = ins["q"], ins["k"], ins["v"], ins["dout"]
+            self.o, self.lse = bd.attn_fwd(q, k, v, causal=w.causal)
+            self.flops, self.bytes = acc.workload_work(w)
+            self.call, _ = bd.prepare_bwd(q, k, v, self.o, self.lse, do, causal=w.causal)
         else:
             sl = ins["seqlens"]
             self.o = torch.empty_like(ins["q"])
@@ -149,17 +156,48 @@ def cpu_baseline(part, budget_s):
         heads += 1
     dt = time.perf_counter() - t0
     flops = 4 * w.d * pairs * heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"{w.name}: batch 0, {heads} of {w.Hq} query heads, all {w.Nq} rows "
+                      f"(fp64 NumPy, S and P materialised), {dt:.1f} s",
+            "seconds": dt}
+
+
+def cpu_baseline_bwd(part, budget_s):
+    """The gradient oracle, as it is, on a bounded sample of a backward
+    workload: one query head (with its KV head) of batch 0 at a time, until the
+    time budget is spent."""
+    import oracle
+    from exact_io_aware_attn_amd import accounting as acc
+
+    w = part.w
+    ins = part.ins
+    f64 = lambda t: t.to("cpu").double().numpy()
+    G = w.Hq // w.Hkv
+    pairs = acc.attended_pairs(w.Nq, w.Nk, causal=w.causal)
+    heads = 0
+    t0 = time.perf_counter()
+    while heads < w.Hq and (heads == 0 or time.perf_counter() - t0 < budget_s):
+        h, hk = heads, heads // G
+        oracle.attention_backward(f64(ins["q"][:1, :, h:h + 1]), f64(ins["k"][:1, :, hk:hk + 1]),
+                                  f64(ins["v"][:1, :, hk:hk + 1]), f64(ins["dout"][:1, :, h:h + 1]),
+                                  w.scale, causal=w.causal)
+        heads += 1
+    dt = time.perf_counter() - t0
+    flops = 10 * w.d * pairs * heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"{w.name}: batch 0, {heads} of {w.Hq} query heads, all {w.Nq} rows "
+                      f"(fp64 NumPy, S, P, dP and dS materialised), {dt:.1f} s",
+            "seconds": dt}
+
+
+def _threads():
     threads = None
     try:
         from threadpoolctl import threadpool_info
         threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
     except Exception:
         pass
-    cores = threads or len(os.sched_getaffinity(0))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{w.name}: batch 0, {heads} of {w.Hq} query heads, all {w.Nq} rows "
-                      f"(fp64 NumPy, S and P materialised), {dt:.1f} s",
-            "seconds": dt}
+    return threads or len(os.sched_getaffinity(0))
 
 
 def main():
@@ -233,7 +271,9 @@ def main():
 
     main_p = parts[0]
     out = {"metric": "fwd attn TFLOP/s & %MFMA peak (prefill); KV-read GB/s & %HBM peak (decode)"}
-    if main_p.kind == "prefill":
+    if main_p.kind == "backward":
+        out["metric"] = "bwd attn TFLOP/s (10 d FLOPs per attended pair) & %MFMA peak"
+    if main_p.kind in ("prefill", "backward"):
         tflops = main_p.flops / (ms_avg[0] * 1e-3) / 1e12
         peak = MFMA_BF16_PEAK if main_p.w.dtype == "bf16" else FP32_PEAK
         out.update(value=tflops, unit="TFLOP/s")
@@ -272,6 +312,8 @@ def main():
                                   "traffic": measured_traffic("decode")}
     if not args.no_cpu_baseline and main_p.kind == "prefill":
         out["cpu_baseline"] = cpu_baseline(main_p, args.cpu_seconds)
+    elif not args.no_cpu_baseline and main_p.kind == "backward":
+        out["cpu_baseline"] = cpu_baseline_bwd(main_p, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out))
