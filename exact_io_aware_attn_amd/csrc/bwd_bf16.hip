@@ -193,60 +193,95 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
   const int tr_ch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int tr_half = 4 * (lane & 1);
 
+  // one 32-query block qb of the tile: products, softmax, gradient products
+  auto scores = [&](const __bf16* sq, const __bf16* sg, int qb, f32x16& s, f32x16& dp)
+      __attribute__((always_inline)) {
+    s = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      s = mfma32(row_frag<D, true>(sq, qb, t, qc, h), kf[t], s);
+      dp = mfma32(row_frag<D, true>(sg, qb, t, qc, h), vf[t], dp);
+    }
+  };
+  // P = exp2(c s - lse2) into s and dS = P (dP - D) into dp, rows 8j + 4h + i
+  auto softmax = [&](const float* ss, int qb, int qs, bool masked, f32x16& s, f32x16& dp)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 l4 = *(const f32x4*)(ss + 32 * qb + 8 * j + 4 * h);
+      const f32x4 d4 = *(const f32x4*)(ss + BT + 32 * qb + 8 * j + 4 * h);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * j + i;
+        float pr = ex2(__builtin_fmaf(s[r], c, -l4[i]));
+        if (CAUSAL && masked) {
+          const int q = qs + 8 * j + 4 * h + i;
+          pr = key <= q + p.causal_off ? pr : 0.f;
+        }
+        s[r] = pr;
+        dp[r] = pr * (dp[r] - d4[i]);
+      }
+    }
+  };
+  auto grads = [&](const __bf16* sq, const __bf16* sg, int qb, const f32x16& s, const f32x16& dp)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) {
+      const int u = 2 * qb + uu;
+      const int o8 = 8 * uu;
+      const bf16x8 pf = cvt8(s[o8 + 0], s[o8 + 1], s[o8 + 2], s[o8 + 3], s[o8 + 4], s[o8 + 5],
+                             s[o8 + 6], s[o8 + 7]);
+      const bf16x8 df = cvt8(dp[o8 + 0], dp[o8 + 1], dp[o8 + 2], dp[o8 + 3], dp[o8 + 4],
+                             dp[o8 + 5], dp[o8 + 6], dp[o8 + 7]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        dvacc[mb] = mfma32(tr_frag<D>(sg, u, mb, tr_row, tr_ch, tr_half), pf, dvacc[mb]);
+        dkacc[mb] = mfma32(tr_frag<D>(sq, u, mb, tr_row, tr_ch, tr_half), df, dkacc[mb]);
+      }
+    }
+  };
+
   auto body = [&](int st, int buf) {
     const int g = st / n_qt;
     const int r0 = qb0 + (st - g * n_qt) * BT;
     const __bf16* sq = sQ[buf];
     const __bf16* sg = sG[buf];
     const float* ss = sSt[buf];
+    // per 32-query block: 0 no pair visible, 1 all visible, 2 apply the causal rule
+    int state[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int qs = r0 + 32 * qb;  // first query row of the block
-      // 0: no pair visible, 1: all visible, 2: apply the causal rule
-      int state = 1;
-      if (qs >= p.Nq) state = 0;
+      const int qs = r0 + 32 * qb;
+      state[qb] = 1;
+      if (qs >= p.Nq) state[qb] = 0;
       else if (CAUSAL) {
-        if (qs + 31 + p.causal_off < k0w) state = 0;
-        else if (qs + p.causal_off < k0w + 31) state = 2;
+        if (qs + 31 + p.causal_off < k0w) state[qb] = 0;
+        else if (qs + p.causal_off < k0w + 31) state[qb] = 2;
       }
-      if (state == 0) continue;
-      f32x16 s = {}, dp = {};
+    }
+    if (D == 128 && state[0] == 1 && state[1] == 1) {
+      // both blocks fully visible: straight-line, both blocks' score products
+      // first, so block 0's softmax runs while block 1's products are in the
+      // matrix pipe and block 1's softmax under block 0's gradient products
+      // (d = 128 runs one wave per SIMD: no other wave hides the softmax;
+      // at d = 64 two waves share a SIMD and the extra registers cost more)
+      f32x16 s0, dp0, s1, dp1;
+      scores(sq, sg, 0, s0, dp0);
+      scores(sq, sg, 1, s1, dp1);
+      softmax(ss, 0, r0, false, s0, dp0);
+      grads(sq, sg, 0, s0, dp0);
+      softmax(ss, 1, r0 + 32, false, s1, dp1);
+      grads(sq, sg, 1, s1, dp1);
+      return;
+    }
 #pragma unroll
-      for (int t = 0; t < KSTEPS; ++t) {
-        s = mfma32(row_frag<D, true>(sq, qb, t, qc, h), kf[t], s);
-        dp = mfma32(row_frag<D, true>(sg, qb, t, qc, h), vf[t], dp);
-      }
-      // P = exp2(c s - lse2) and dS = P (dP - D) per row 8j + 4h + i
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 l4 = *(const f32x4*)(ss + 32 * qb + 8 * j + 4 * h);
-        const f32x4 d4 = *(const f32x4*)(ss + BT + 32 * qb + 8 * j + 4 * h);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * j + i;
-          float pr = ex2(__builtin_fmaf(s[r], c, -l4[i]));
-          if (CAUSAL && state == 2) {
-            const int q = qs + 8 * j + 4 * h + i;
-            pr = key <= q + p.causal_off ? pr : 0.f;
-          }
-          s[r] = pr;
-          dp[r] = pr * (dp[r] - d4[i]);
-        }
-      }
-#pragma unroll
-      for (int uu = 0; uu < 2; ++uu) {
-        const int u = 2 * qb + uu;
-        const int o8 = 8 * uu;
-        const bf16x8 pf = cvt8(s[o8 + 0], s[o8 + 1], s[o8 + 2], s[o8 + 3], s[o8 + 4], s[o8 + 5],
-                               s[o8 + 6], s[o8 + 7]);
-        const bf16x8 df = cvt8(dp[o8 + 0], dp[o8 + 1], dp[o8 + 2], dp[o8 + 3], dp[o8 + 4],
-                               dp[o8 + 5], dp[o8 + 6], dp[o8 + 7]);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          dvacc[mb] = mfma32(tr_frag<D>(sg, u, mb, tr_row, tr_ch, tr_half), pf, dvacc[mb]);
-          dkacc[mb] = mfma32(tr_frag<D>(sq, u, mb, tr_row, tr_ch, tr_half), df, dkacc[mb]);
-        }
-      }
+    for (int qb = 0; qb < 2; ++qb) {
+      if (state[qb] == 0) continue;
+      f32x16 s, dp;
+      scores(sq, sg, qb, s, dp);
+      softmax(ss, qb, r0 + 32 * qb, state[qb] == 2, s, dp);
+      grads(sq, sg, qb, s, dp);
     }
   };
 
