@@ -242,6 +242,112 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
     }
   };
 
+  // Both 32-query blocks of a tile fully visible (d = 128, one wave per SIMD,
+  // so the wave's own issue order decides what overlaps): four straight-line
+  // stages with a fixed order (sched_barrier between steps), each MFMA step
+  // carrying one element of softmax work and the LDS reads of the operands
+  // two products ahead --
+  //   A. block 0's S and dP products
+  //   B. block 1's S and dP products, block 0's softmax
+  //   C. block 0's dV and dK products, block 1's softmax
+  //   D. block 1's dV and dK products
+  constexpr int NPB = 2 * KSTEPS;  // products per stage (16 at d = 128)
+  constexpr int LEAD = 2;
+  auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+  auto fast = [&](const __bf16* sq, const __bf16* sg, const float* ss)
+      __attribute__((always_inline)) {
+    // operand i of a score stage: S (even, Q rows) or dP (odd, dO rows)
+    auto sc_op = [&](int qb, int i) __attribute__((always_inline)) {
+      return row_frag<D, true>((i & 1) ? sg : sq, qb, i >> 1, qc, h);
+    };
+    // operand i of a gradient stage: dV (even, dO^T) or dK (odd, Q^T), step
+    // u = 2 qb + i / (2 MB), column block (i % (2 MB)) / 2
+    auto gr_op = [&](int qb, int i) __attribute__((always_inline)) {
+      return tr_frag<D>((i & 1) ? sq : sg, 2 * qb + i / (2 * MB), (i % (2 * MB)) >> 1, tr_row,
+                        tr_ch, tr_half);
+    };
+    f32x4 st4[2][2][4];  // [block][lse2, dsum][j]
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        st4[qb][0][j] = *(const f32x4*)(ss + 32 * qb + 8 * j + 4 * h);
+        st4[qb][1][j] = *(const f32x4*)(ss + BT + 32 * qb + 8 * j + 4 * h);
+      }
+    f32x16 sb[2], db[2];
+    // softmax step j of block qb: P of element j, dS of element j - 1
+    auto sm_step = [&](int qb, int j) __attribute__((always_inline)) {
+      if (j < 16) sb[qb][j] = ex2(__builtin_fmaf(sb[qb][j], c, -st4[qb][0][j >> 2][j & 3]));
+      if (j >= 1) {
+        const int e = j - 1;
+        db[qb][e] = sb[qb][e] * (db[qb][e] - st4[qb][1][e >> 2][e & 3]);
+      }
+    };
+    bf16x8 op[NPB];
+#pragma unroll
+    for (int i = 0; i < LEAD; ++i) op[i] = sc_op(0, i);
+    sb[0] = f32x16{};
+    db[0] = f32x16{};
+    sb[1] = f32x16{};
+    db[1] = f32x16{};
+    fence();
+    // A
+#pragma unroll
+    for (int i = 0; i < NPB; ++i) {
+      if (i & 1) db[0] = mfma32(op[i], vf[i >> 1], db[0]);
+      else sb[0] = mfma32(op[i], kf[i >> 1], sb[0]);
+      if (i + LEAD < NPB) op[i + LEAD] = sc_op(0, i + LEAD);
+      else op[i + LEAD - NPB] = sc_op(1, i + LEAD - NPB);
+      fence();
+    }
+    // B
+#pragma unroll
+    for (int i = 0; i < NPB; ++i) {
+      if (i & 1) db[1] = mfma32(op[i], vf[i >> 1], db[1]);
+      else sb[1] = mfma32(op[i], kf[i >> 1], sb[1]);
+      if (i + LEAD < NPB) op[i + LEAD] = sc_op(1, i + LEAD);
+      else op[i + LEAD - NPB] = gr_op(0, i + LEAD - NPB);
+      sm_step(0, i);
+      fence();
+    }
+    sm_step(0, 16);
+    bf16x8 pf = cvt8(sb[0][0], sb[0][1], sb[0][2], sb[0][3], sb[0][4], sb[0][5], sb[0][6], sb[0][7]);
+    bf16x8 df = cvt8(db[0][0], db[0][1], db[0][2], db[0][3], db[0][4], db[0][5], db[0][6], db[0][7]);
+    fence();
+    // C
+#pragma unroll
+    for (int i = 0; i < NPB; ++i) {
+      if (i == 2 * MB) {
+        pf = cvt8(sb[0][8], sb[0][9], sb[0][10], sb[0][11], sb[0][12], sb[0][13], sb[0][14], sb[0][15]);
+        df = cvt8(db[0][8], db[0][9], db[0][10], db[0][11], db[0][12], db[0][13], db[0][14], db[0][15]);
+      }
+      const int mb = (i % (2 * MB)) >> 1;
+      if (i & 1) dkacc[mb] = mfma32(op[i], df, dkacc[mb]);
+      else dvacc[mb] = mfma32(op[i], pf, dvacc[mb]);
+      if (i + LEAD < NPB) op[i + LEAD] = gr_op(0, i + LEAD);
+      else op[i + LEAD - NPB] = gr_op(1, i + LEAD - NPB);
+      sm_step(1, i);
+      fence();
+    }
+    sm_step(1, 16);
+    pf = cvt8(sb[1][0], sb[1][1], sb[1][2], sb[1][3], sb[1][4], sb[1][5], sb[1][6], sb[1][7]);
+    df = cvt8(db[1][0], db[1][1], db[1][2], db[1][3], db[1][4], db[1][5], db[1][6], db[1][7]);
+    fence();
+    // D
+#pragma unroll
+    for (int i = 0; i < NPB; ++i) {
+      if (i == 2 * MB) {
+        pf = cvt8(sb[1][8], sb[1][9], sb[1][10], sb[1][11], sb[1][12], sb[1][13], sb[1][14], sb[1][15]);
+        df = cvt8(db[1][8], db[1][9], db[1][10], db[1][11], db[1][12], db[1][13], db[1][14], db[1][15]);
+      }
+      const int mb = (i % (2 * MB)) >> 1;
+      if (i & 1) dkacc[mb] = mfma32(op[i], df, dkacc[mb]);
+      else dvacc[mb] = mfma32(op[i], pf, dvacc[mb]);
+      if (i + LEAD < NPB) op[i + LEAD] = gr_op(1, i + LEAD);
+      fence();
+    }
+  };
+
   auto body = [&](int st, int buf) {
     const int g = st / n_qt;
     const int r0 = qb0 + (st - g * n_qt) * BT;
@@ -261,18 +367,7 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
       }
     }
     if (D == 128 && state[0] == 1 && state[1] == 1) {
-      // both blocks fully visible: straight-line, both blocks' score products
-      // first, so block 0's softmax runs while block 1's products are in the
-      // matrix pipe and block 1's softmax under block 0's gradient products
-      // (d = 128 runs one wave per SIMD: no other wave hides the softmax;
-      // at d = 64 two waves share a SIMD and the extra registers cost more)
-      f32x16 s0, dp0, s1, dp1;
-      scores(sq, sg, 0, s0, dp0);
-      scores(sq, sg, 1, s1, dp1);
-      softmax(ss, 0, r0, false, s0, dp0);
-      grads(sq, sg, 0, s0, dp0);
-      softmax(ss, 1, r0 + 32, false, s1, dp1);
-      grads(sq, sg, 1, s1, dp1);
+      fast(sq, sg, ss);
       return;
     }
 #pragma unroll
