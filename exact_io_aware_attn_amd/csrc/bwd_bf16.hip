@@ -242,8 +242,9 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
     }
   };
 
-  // Both 32-query blocks of a tile fully visible (d = 128, one wave per SIMD,
-  // so the wave's own issue order decides what overlaps): four straight-line
+  // Both 32-query blocks of a tile fully visible, d = 128 (one wave per SIMD,
+  // so the wave's own issue order decides what overlaps; at d = 64 two waves
+  // share a SIMD and the fixed order measured slower): four straight-line
   // stages with a fixed order (sched_barrier between steps), each MFMA step
   // carrying one element of softmax work and the LDS reads of the operands
   // two products ahead --
@@ -251,8 +252,9 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
   //   B. block 1's S and dP products, block 0's softmax
   //   C. block 0's dV and dK products, block 1's softmax
   //   D. block 1's dV and dK products
-  constexpr int NPB = 2 * KSTEPS;  // products per stage (16 at d = 128)
+  constexpr int NPB = 2 * KSTEPS;  // products per stage (16 at d = 128, 8 at d = 64)
   constexpr int LEAD = 2;
+  constexpr int SPP = 16 / NPB;    // softmax steps per product (17 steps: the last after)
   auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
   auto fast = [&](const __bf16* sq, const __bf16* sg, const float* ss)
       __attribute__((always_inline)) {
@@ -307,10 +309,12 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
       else sb[1] = mfma32(op[i], kf[i >> 1], sb[1]);
       if (i + LEAD < NPB) op[i + LEAD] = sc_op(1, i + LEAD);
       else op[i + LEAD - NPB] = gr_op(0, i + LEAD - NPB);
-      sm_step(0, i);
+#pragma unroll
+      for (int k = 0; k < SPP; ++k) sm_step(0, i * SPP + k);
       fence();
     }
-    sm_step(0, 16);
+#pragma unroll
+    for (int j = NPB * SPP; j <= 16; ++j) sm_step(0, j);
     bf16x8 pf = cvt8(sb[0][0], sb[0][1], sb[0][2], sb[0][3], sb[0][4], sb[0][5], sb[0][6], sb[0][7]);
     bf16x8 df = cvt8(db[0][0], db[0][1], db[0][2], db[0][3], db[0][4], db[0][5], db[0][6], db[0][7]);
     fence();
@@ -326,10 +330,12 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
       else dvacc[mb] = mfma32(op[i], pf, dvacc[mb]);
       if (i + LEAD < NPB) op[i + LEAD] = gr_op(0, i + LEAD);
       else op[i + LEAD - NPB] = gr_op(1, i + LEAD - NPB);
-      sm_step(1, i);
+#pragma unroll
+      for (int k = 0; k < SPP; ++k) sm_step(1, i * SPP + k);
       fence();
     }
-    sm_step(1, 16);
+#pragma unroll
+    for (int j = NPB * SPP; j <= 16; ++j) sm_step(1, j);
     pf = cvt8(sb[1][0], sb[1][1], sb[1][2], sb[1][3], sb[1][4], sb[1][5], sb[1][6], sb[1][7]);
     df = cvt8(db[1][0], db[1][1], db[1][2], db[1][3], db[1][4], db[1][5], db[1][6], db[1][7]);
     fence();
@@ -501,6 +507,90 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
   const int tr_ch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int tr_half = 4 * (lane & 1);
 
+  // A fully visible tile at d = 128 as four straight-line stages in a fixed
+  // order (sched_barrier between steps; LDS operands two products ahead; at
+  // d = 64 the compiler's own order measured faster):
+  //   A. S^T and dP^T of key block 0
+  //   B. the same for key block 1, with block 0's dS^T elements in between
+  //   C. dQ^T products of block 0, with block 1's dS^T elements in between
+  //   D. dQ^T products of block 1
+  constexpr int NPS = 2 * KSTEPS;  // score-stage products
+  constexpr int NPG = 2 * MB;      // gradient-stage products
+  constexpr int LEAD = 2;
+  constexpr int SPG = (17 + NPG - 1) / NPG;  // softmax steps per gradient product
+  auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+  auto fast = [&](const __bf16* sk, const __bf16* sv) __attribute__((always_inline)) {
+    auto sc_op = [&](int kb, int i) __attribute__((always_inline)) {
+      return (i & 1) ? row_frag<D, false>(sv, kb, i >> 1, qc, h) : row_frag<D, true>(sk, kb, i >> 1, qc, h);
+    };
+    // gradient product i of block kb: step u = 2 kb + i / MB, column block i % MB
+    auto gr_op = [&](int kb, int i) __attribute__((always_inline)) {
+      return tr_frag<D>(sk, 2 * kb + i / MB, i % MB, tr_row, tr_ch, tr_half);
+    };
+    f32x16 sb[2], db[2];
+    auto sm_step = [&](int kb, int j) __attribute__((always_inline)) {
+      if (j < 16) sb[kb][j] = ex2(__builtin_fmaf(sb[kb][j], c, -lse2));
+      if (j >= 1 && j <= 16) db[kb][j - 1] = sb[kb][j - 1] * (db[kb][j - 1] - dsum);
+    };
+    bf16x8 op[NPS];
+#pragma unroll
+    for (int i = 0; i < LEAD; ++i) op[i] = sc_op(0, i);
+    sb[0] = f32x16{};
+    db[0] = f32x16{};
+    sb[1] = f32x16{};
+    db[1] = f32x16{};
+    fence();
+    // A
+#pragma unroll
+    for (int i = 0; i < NPS; ++i) {
+      if (i & 1) db[0] = mfma32(op[i], gf[i >> 1], db[0]);
+      else sb[0] = mfma32(op[i], qf[i >> 1], sb[0]);
+      if (i + LEAD < NPS) op[i + LEAD] = sc_op(0, i + LEAD);
+      else op[i + LEAD - NPS] = sc_op(1, i + LEAD - NPS);
+      fence();
+    }
+    // B
+#pragma unroll
+    for (int i = 0; i < NPS; ++i) {
+      if (i & 1) db[1] = mfma32(op[i], gf[i >> 1], db[1]);
+      else sb[1] = mfma32(op[i], qf[i >> 1], sb[1]);
+      if (i + LEAD < NPS) op[i + LEAD] = sc_op(1, i + LEAD);
+      else op[i + LEAD - NPS] = gr_op(0, i + LEAD - NPS);
+#pragma unroll
+      for (int k = 0; k < 16 / NPS; ++k) sm_step(0, i * (16 / NPS) + k);
+      fence();
+    }
+    sm_step(0, 16);
+    bf16x8 df = cvt8(db[0][0], db[0][1], db[0][2], db[0][3], db[0][4], db[0][5], db[0][6], db[0][7]);
+    fence();
+    // C
+#pragma unroll
+    for (int i = 0; i < NPG; ++i) {
+      if (i == MB)
+        df = cvt8(db[0][8], db[0][9], db[0][10], db[0][11], db[0][12], db[0][13], db[0][14], db[0][15]);
+      acc[i % MB] = mfma32(op[i], df, acc[i % MB]);
+      if (i + LEAD < NPG) op[i + LEAD] = gr_op(0, i + LEAD);
+      else op[i + LEAD - NPG] = gr_op(1, i + LEAD - NPG);
+#pragma unroll
+      for (int k = 0; k < SPG; ++k)
+        if (i * SPG + k <= 16) sm_step(1, i * SPG + k);
+      fence();
+    }
+#pragma unroll
+    for (int j = NPG * SPG; j <= 16; ++j) sm_step(1, j);
+    df = cvt8(db[1][0], db[1][1], db[1][2], db[1][3], db[1][4], db[1][5], db[1][6], db[1][7]);
+    fence();
+    // D
+#pragma unroll
+    for (int i = 0; i < NPG; ++i) {
+      if (i == MB)
+        df = cvt8(db[1][8], db[1][9], db[1][10], db[1][11], db[1][12], db[1][13], db[1][14], db[1][15]);
+      acc[i % MB] = mfma32(op[i], df, acc[i % MB]);
+      if (i + LEAD < NPG) op[i + LEAD] = gr_op(1, i + LEAD);
+      fence();
+    }
+  };
+
   auto body = [&](int t, int buf) {
     const int k0 = t * BT;
     int state = 1;  // 0: nothing visible, 1: all visible, 2: apply the rules
@@ -515,6 +605,10 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
     if (state == 0) return;
     const __bf16* sk = sK[buf];
     const __bf16* sv = sV[buf];
+    if (D == 128 && state == 1) {
+      fast(sk, sv);
+      return;
+    }
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
