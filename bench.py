@@ -24,7 +24,8 @@ gpt2-causal, gpt2-medium-causal, llama3-8b-gqa-causal-8k, gqa-decode-b64,
 video-frames-16x880 (online), video-frames-16x880-fixed,
 video-frames-16x880-centered, tiny-f32, and the backward pass (attn_bwd, with
 O and the LSE from one attn_fwd call made before the timed steps; 10 d FLOPs
-per attended pair): llama3-8b-gqa-causal-8k-bwd, gpt2-medium-causal-bwd.
+per attended pair): llama3-8b-gqa-causal-8k-bwd, gpt2-medium-causal-bwd,
+video-frames-16x880-bwd.
 """
 
 import argparse
@@ -117,9 +118,13 @@ class Part:
                 softmax=self.softmax, out=self.o, lse_out=self.lse, workspace=self.ws)
         elif w.kind == "backward":
             q, k, v, do = ins["q"], ins["k"], ins["v"], ins["dout"]
-            self.o, self.lse = bd.attn_fwd(q, k, v, causal=w.causal)
-            self.flops, self.bytes = acc.workload_work(w)
-            self.call, _ = bd.prepare_bwd(q, k, v, self.o, self.lse, do, causal=w.causal)
+            bm = ins.get("block_mask")
+            self.bm = None if bm is None else torch.from_numpy(bm).to(dev)
+            blk = (w.block, w.block) if bm is not None else None
+            self.o, self.lse = bd.attn_fwd(q, k, v, causal=w.causal, block_mask=self.bm, block=blk)
+            self.flops, self.bytes = acc.workload_work(w, block_mask=bm)
+            self.call, _ = bd.prepare_bwd(q, k, v, self.o, self.lse, do, causal=w.causal,
+                                          block_mask=self.bm, block=blk)
         else:
             sl = ins["seqlens"]
             self.o = torch.empty_like(ins["q"])
@@ -173,14 +178,19 @@ def cpu_baseline_bwd(part, budget_s):
     ins = part.ins
     f64 = lambda t: t.to("cpu").double().numpy()
     G = w.Hq // w.Hkv
-    pairs = acc.attended_pairs(w.Nq, w.Nk, causal=w.causal)
+    bm = ins.get("block_mask")
+    kw = dict(causal=w.causal)
+    if bm is not None:
+        kw.update(block_mask=bm, block_q=w.block, block_k=w.block)
+    pairs = acc.attended_pairs(w.Nq, w.Nk, causal=w.causal, block_mask=bm,
+                               block_q=w.block or None, block_k=w.block or None)
     heads = 0
     t0 = time.perf_counter()
     while heads < w.Hq and (heads == 0 or time.perf_counter() - t0 < budget_s):
         h, hk = heads, heads // G
         oracle.attention_backward(f64(ins["q"][:1, :, h:h + 1]), f64(ins["k"][:1, :, hk:hk + 1]),
                                   f64(ins["v"][:1, :, hk:hk + 1]), f64(ins["dout"][:1, :, h:h + 1]),
-                                  w.scale, causal=w.causal)
+                                  w.scale, **kw)
         heads += 1
     dt = time.perf_counter() - t0
     flops = 10 * w.d * pairs * heads

@@ -62,7 +62,7 @@ def library():
     lib.attn_decode.restype = I
     lib.attn_bwd_workspace_bytes.argtypes = [I, I, I]
     lib.attn_bwd_workspace_bytes.restype = Z
-    lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I,
+    lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, I, I,
                              ctypes.POINTER(_Strides), P, Z, P]
     lib.attn_bwd.restype = I
     _lib = lib
@@ -241,7 +241,7 @@ def prepare_decode(q, k_cache, v_cache, seqlens, *, scale=None, kv_splits=0, ret
     return PreparedCall(library().attn_decode, args, "attn_decode", keep), o, lse
 
 
-def _bwd_setup(q, k, v, o, lse, dout, causal, scale, dq, dk, dv, workspace):
+def _bwd_setup(q, k, v, o, lse, dout, causal, block_mask, block, scale, dq, dk, dv, workspace):
     _check_gpu(q, k, v, o, lse, dout)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or o.shape != q.shape \
             or dout.shape != q.shape:
@@ -263,26 +263,36 @@ def _bwd_setup(q, k, v, o, lse, dout, causal, scale, dq, dk, dv, workspace):
     st = (_Strides * 8)(*[_strides4(t) for t in (q, k, v, o, dout, dq, dk, dv)])
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     mask_kind = MIATTN_MASK_CAUSAL if causal else MIATTN_MASK_NONE
+    bm = None
+    bq = bk = 0
+    if block_mask is not None:
+        mask_kind |= MIATTN_MASK_BLOCK
+        bq, bk = block
+        if isinstance(block_mask, np.ndarray):
+            block_mask = torch.from_numpy(np.ascontiguousarray(block_mask, dtype=np.uint8))
+        bm = block_mask.to(device=dev, dtype=torch.uint8).contiguous()
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
-            _ptr(dv), _dtype_code(q), B, Hq, Hkv, Nq, Nk, d, scale, mask_kind, st,
-            _ptr(workspace), ws_bytes, _stream(dev))
-    return args, (dq, dk, dv), (q, k, v, o, lse, dout, dq, dk, dv, workspace, st)
+            _ptr(dv), _dtype_code(q), B, Hq, Hkv, Nq, Nk, d, scale, mask_kind, _ptr(bm), bq, bk,
+            st, _ptr(workspace), ws_bytes, _stream(dev))
+    return args, (dq, dk, dv), (q, k, v, o, lse, dout, dq, dk, dv, bm, workspace, st)
 
 
-def attn_bwd(q, k, v, o, lse, dout, *, causal=False, scale=None, dq=None, dk=None, dv=None,
-             workspace=None):
+def attn_bwd(q, k, v, o, lse, dout, *, causal=False, block_mask=None, block=None, scale=None,
+             dq=None, dk=None, dv=None, workspace=None):
     """Gradients of attention with respect to q, k, v (bf16 GPU tensors) for the
-    upstream gradient dout, given the forward's o and lse [B,Hq,Nq] (float32).
-    Returns (dq, dk, dv)."""
-    args, grads, _ = _bwd_setup(q, k, v, o, lse, dout, causal, scale, dq, dk, dv, workspace)
+    upstream gradient dout, given the forward's o and lse [B,Hq,Nq] (float32) and
+    the forward's mask. Returns (dq, dk, dv)."""
+    args, grads, _ = _bwd_setup(q, k, v, o, lse, dout, causal, block_mask, block, scale, dq, dk,
+                                dv, workspace)
     rc = library().attn_bwd(*args)
     if rc != 0:
         raise MiattnError(rc, "attn_bwd")
     return grads
 
 
-def prepare_bwd(q, k, v, o, lse, dout, *, causal=False, scale=None, dq=None, dk=None, dv=None,
-                workspace=None):
+def prepare_bwd(q, k, v, o, lse, dout, *, causal=False, block_mask=None, block=None, scale=None,
+                dq=None, dk=None, dv=None, workspace=None):
     """attn_bwd as a PreparedCall: returns (call, (dq, dk, dv))."""
-    args, grads, keep = _bwd_setup(q, k, v, o, lse, dout, causal, scale, dq, dk, dv, workspace)
+    args, grads, keep = _bwd_setup(q, k, v, o, lse, dout, causal, block_mask, block, scale, dq,
+                                   dk, dv, workspace)
     return PreparedCall(library().attn_bwd, args, "attn_bwd", keep), grads

@@ -273,6 +273,7 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq) {
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, int dtype, int B, int Hq,
              int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
+             const uint8_t* block_mask, int block_q, int block_k,
              const miattn_strides* strides, void* workspace, size_t workspace_bytes,
              void* stream) {
   if (dtype != MIATTN_BF16) return MIATTN_ERR_UNSUPPORTED;
@@ -281,8 +282,14 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (d != 64 && d != 128) return MIATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(scale) || !(scale > 0.f)) return MIATTN_ERR_ARG;
   if (mask_kind < 0 || mask_kind > (MIATTN_MASK_CAUSAL | MIATTN_MASK_BLOCK)) return MIATTN_ERR_ARG;
-  if (mask_kind & MIATTN_MASK_BLOCK) return MIATTN_ERR_UNSUPPORTED;
+  const bool block = (mask_kind & MIATTN_MASK_BLOCK) != 0;
+  if (block) {
+    if (block_q <= 0 || block_k <= 0 || block_q % 16 != 0 || block_k % 16 != 0)
+      return MIATTN_ERR_SHAPE;
+    if (Nq % block_q != 0 || Nk % block_k != 0) return MIATTN_ERR_SHAPE;
+  }
   if (B == 0 || (Nq == 0 && Nk == 0)) return MIATTN_OK;
+  if (block && Nq > 0 && Nk > 0 && block_mask == nullptr) return MIATTN_ERR_NULL;
   if (Nq > 0 && (q == nullptr || o == nullptr || dout == nullptr || lse == nullptr || dq == nullptr))
     return MIATTN_ERR_NULL;
   if (Nk > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
@@ -326,9 +333,13 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.causal_off = Nk - Nq;
+  p.block_mask = block ? block_mask : nullptr;
+  p.block_q = block ? block_q : 0;
+  p.block_k = block ? block_k : 0;
+  p.nkb = block ? Nk / block_k : 0;
   p.npad = (Nq + 63) / 64 * 64;
   p.stats = (float*)workspace;
-  hipError_t e = miattn::launch_bwd_bf16(p, d, (mask_kind & MIATTN_MASK_CAUSAL) != 0,
+  hipError_t e = miattn::launch_bwd_bf16(p, d, (mask_kind & MIATTN_MASK_CAUSAL) != 0, block,
                                          (hipStream_t)stream);
   return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;
 }

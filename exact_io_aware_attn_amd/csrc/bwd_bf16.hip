@@ -59,6 +59,23 @@ __device__ __forceinline__ uint32_t span(int n, int64_t stride) {
   return n > 0 ? (uint32_t)(((int64_t)(n - 1) * stride + D) * 2) : 0u;
 }
 
+// Block mask over rows [q_lo, q_hi] x keys [k_lo, k_hi] (inside Nq x Nk):
+// 0 every pair excluded, 1 every pair included, 2 mixed. Uniform per wave.
+__device__ __forceinline__ int block_state(const BwdParams& p, int q_lo, int q_hi, int k_lo,
+                                           int k_hi) {
+  bool any = false, all = true;
+  for (int qb = q_lo / p.block_q; qb <= q_hi / p.block_q; ++qb)
+    for (int kb = k_lo / p.block_k; kb <= k_hi / p.block_k; ++kb) {
+      const bool live = p.block_mask[(int64_t)qb * p.nkb + kb] != 0;
+      any |= live;
+      all &= live;
+    }
+  return !any ? 0 : all ? 1 : 2;
+}
+__device__ __forceinline__ bool pair_live(const BwdParams& p, int q, int key) {
+  return p.block_mask[(int64_t)(q / p.block_q) * p.nkb + key / p.block_k] != 0;
+}
+
 // ---- D_i = dO_i . O_i (fp32) and LSE_i * log2(e), per (batch, head, row);
 // rows Nq .. npad-1 get D = 0 and +inf (their weights exp2(s - inf) are 0).
 // D/8 lanes per row, 16 bytes each.
@@ -99,7 +116,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const BwdParams p) {
 // dK^T += Q^T dS, whose A operands are transposed reads of the dO and Q tiles.
 // d = 128 holds K, V and both accumulators (192 registers) plus the tile's
 // S and dP: one wave per SIMD, so nothing spills.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BLOCK>
 __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(const BwdParams p) {
   constexpr int CH = D / 8;
   constexpr int KSTEPS = D / 16;
@@ -215,9 +232,12 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * j + i;
         float pr = ex2(__builtin_fmaf(s[r], c, -l4[i]));
-        if (CAUSAL && masked) {
+        if ((CAUSAL || BLOCK) && masked) {
           const int q = qs + 8 * j + 4 * h + i;
-          pr = key <= q + p.causal_off ? pr : 0.f;
+          bool ok = true;
+          if (CAUSAL) ok = key <= q + p.causal_off;
+          if (BLOCK) ok = ok && q < p.Nq && key_ok && pair_live(p, q, key);
+          pr = ok ? pr : 0.f;
         }
         s[r] = pr;
         dp[r] = pr * (dp[r] - d4[i]);
@@ -366,10 +386,14 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
     for (int qb = 0; qb < 2; ++qb) {
       const int qs = r0 + 32 * qb;
       state[qb] = 1;
-      if (qs >= p.Nq) state[qb] = 0;
+      if (qs >= p.Nq || k0w >= p.Nk) state[qb] = 0;
       else if (CAUSAL) {
         if (qs + 31 + p.causal_off < k0w) state[qb] = 0;
         else if (qs + p.causal_off < k0w + 31) state[qb] = 2;
+      }
+      if (BLOCK && state[qb] != 0) {
+        const int bs = block_state(p, qs, min(qs + 31, p.Nq - 1), k0w, min(k0w + 31, p.Nk - 1));
+        state[qb] = bs == 0 ? 0 : (bs == 2 ? 2 : state[qb]);
       }
     }
     if (D == 128 && state[0] == 1 && state[1] == 1) {
@@ -422,7 +446,7 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
 // dP^T = V dO^T come out with lane (c, h) holding query c for the 16 keys
 // 8*(r/4) + 4h + r%4 of a 32-key block; dS^T in that layout is the B operand
 // of dQ^T += K^T dS^T, whose A operand is a transposed read of the K tile.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BLOCK>
 __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
   constexpr int CH = D / 8;
   constexpr int KSTEPS = D / 16;
@@ -601,6 +625,10 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
         else if (k0 + BT - 1 > q0 + p.causal_off) state = 2;
       }
       if (state == 1 && k0 + BT > p.Nk) state = 2;
+      if (BLOCK && state != 0) {
+        const int bs = block_state(p, q0, wave_last, k0, min(k0 + BT - 1, p.Nk - 1));
+        state = bs == 0 ? 0 : (bs == 2 ? 2 : state);
+      }
     }
     if (state == 0) return;
     const __bf16* sk = sK[buf];
@@ -630,6 +658,7 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
           const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
           bool ok = kk < p.Nk;
           if (CAUSAL) ok = ok && kk <= qrow + p.causal_off;
+          if (BLOCK) ok = ok && row_ok && pair_live(p, qrow, kk);
           pr = ok ? pr : 0.f;
         }
         dp[kb][r] = pr * (dp[kb][r] - dsum);
@@ -671,7 +700,7 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BLOCK>
 hipError_t launch(const BwdParams& p, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.Hq * p.npad;
   if (rows > 0) {
@@ -681,18 +710,23 @@ hipError_t launch(const BwdParams& p, hipStream_t s) {
   }
   const int64_t nkw = (int64_t)((p.Nk + 127) / 128) * p.B * p.Hkv;
   if (nkw > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)nkw), dim3(64 * NW), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, BLOCK>), dim3((unsigned)nkw), dim3(64 * NW), 0, s, p);
   const int64_t nqw = (int64_t)((p.Nq + 127) / 128) * p.B * p.Hq;
   if (nqw > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)nqw), dim3(64 * NW), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, BLOCK>), dim3((unsigned)nqw), dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t s) {
-  if (d == 64) return causal ? launch<64, true>(p, s) : launch<64, false>(p, s);
-  return causal ? launch<128, true>(p, s) : launch<128, false>(p, s);
+template <int D>
+hipError_t launch_d(const BwdParams& p, bool causal, bool block, hipStream_t s) {
+  if (block) return causal ? launch<D, true, true>(p, s) : launch<D, false, true>(p, s);
+  return causal ? launch<D, true, false>(p, s) : launch<D, false, false>(p, s);
+}
+
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, bool block, hipStream_t s) {
+  return d == 64 ? launch_d<64>(p, causal, block, s) : launch_d<128>(p, causal, block, s);
 }
 
 }  // namespace miattn

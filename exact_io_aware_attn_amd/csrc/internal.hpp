@@ -98,6 +98,8 @@ struct BwdParams {
   float scale;        // softmax scale on q . k
   float scale_log2;   // scale * log2(e)
   int causal_off;     // Nk - Nq
+  const uint8_t* block_mask;  // [Nq / block_q][nkb] or nullptr
+  int block_q, block_k, nkb;
   int npad;           // Nq rounded up to 64
   float* stats;       // [2][B*Hq][npad]: lse * log2(e) (+inf past Nq), rowsum(dO * O) (0 past Nq)
 };
@@ -112,7 +114,7 @@ hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, bool block,
 hipError_t launch_kstats(const KStatParams& p, int d, bool bf16, bool centred,
                          hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t s);
-hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, bool block, hipStream_t s);
 
 inline int64_t align16(int64_t n) { return (n + 15) & ~(int64_t)15; }
 // workspace bytes of the segment table of an Nq-row mask with block_q rows per block

@@ -68,6 +68,9 @@ WORKLOADS = {
     "gpt2-medium-causal-bwd": Workload("gpt2-medium-causal-bwd", "backward", B=64, Hq=16,
                                        Hkv=16, Nq=1024, Nk=1024, d=64, dtype="bf16",
                                        causal=True, seed=8),
+    "video-frames-16x880-bwd": Workload("video-frames-16x880-bwd", "backward", B=1, Hq=24,
+                                        Hkv=24, Nq=14080, Nk=14080, d=128, dtype="bf16",
+                                        seed=9, frames=16, frame_len=880, block=80),
     "video-frames-16x880": Workload("video-frames-16x880", "prefill", B=1, Hq=24,
                                     Hkv=24, Nq=14080, Nk=14080, d=128, dtype="bf16",
                                     seed=5, frames=16, frame_len=880, block=80,
@@ -150,7 +153,10 @@ def workload_inputs(w: Workload, device="cpu"):
     if w.kind == "backward":
         q, k, v, do = backward_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.torch_dtype,
                                       w.seed, device)
-        return dict(q=q, k=k, v=v, dout=do)
+        out = dict(q=q, k=k, v=v, dout=do)
+        if w.frames:
+            out["block_mask"] = frame_block_mask(w.frames, w.frame_len, w.block)
+        return out
     if w.kind == "prefill":
         q, k, v = prefill_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.torch_dtype,
                                  w.seed, device)

@@ -178,8 +178,9 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
  *             rounded to bf16 for the products that consume them)
  * d           64 or 128
  * scale       > 0 and finite, the forward's scale
- * mask_kind   MIATTN_MASK_NONE or MIATTN_MASK_CAUSAL (same rule as attn_fwd);
- *             BLOCK returns MIATTN_ERR_UNSUPPORTED
+ * mask_kind, block_mask, block_q, block_k  the forward's mask, same meaning
+ *             and limits as in attn_fwd (block sizes multiples of 16 dividing
+ *             Nq and Nk); pairs it excludes get no gradient
  * strides     NULL (packed) or an array of 8: q, k, v, o, dout, dq, dk, dv
  * workspace   device, at least attn_bwd_workspace_bytes(B, Hq, Nq) bytes,
  *             owned by the caller, overwritten by the call
@@ -189,6 +190,7 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, int dtype, int B, int Hq,
              int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
+             const uint8_t* block_mask, int block_q, int block_k,
              const miattn_strides* strides, void* workspace, size_t workspace_bytes,
              void* stream);
 

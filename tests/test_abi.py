@@ -127,19 +127,23 @@ def test_bwd_workspace_size():
 
 def _bwd(**kw):
     a = dict(q=16, k=16, v=16, o=16, dout=16, lse=16, dq=16, dk=16, dv=16, dtype=0, B=2, Hq=4,
-             Hkv=2, Nq=100, Nk=80, d=128, scale=0.1, mask_kind=1, ws=16, ws_bytes=1 << 20)
+             Hkv=2, Nq=96, Nk=80, d=128, scale=0.1, mask_kind=1, block_mask=None, block_q=0,
+             block_k=0, ws=16, ws_bytes=1 << 20)
     a.update(kw)
     P = ctypes.c_void_p
     return bd.library().attn_bwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["o"]), P(a["dout"]),
                                  P(a["lse"]), P(a["dq"]), P(a["dk"]), P(a["dv"]), a["dtype"],
                                  a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"],
-                                 a["mask_kind"], None, P(a["ws"]), a["ws_bytes"], None)
+                                 a["mask_kind"], P(a["block_mask"]), a["block_q"], a["block_k"],
+                                 None, P(a["ws"]), a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=1), 3), (dict(d=96), 3), (dict(Hq=3), 2), (dict(B=-1), 2), (dict(Nk=-1), 2),
     (dict(scale=0.0), 6), (dict(scale=float("inf")), 6), (dict(mask_kind=4), 6),
-    (dict(mask_kind=2), 3), (dict(mask_kind=3), 3),
+    (dict(mask_kind=2, block_q=32, block_k=16), 1),            # block mask pointer missing
+    (dict(mask_kind=3, block_mask=16, block_q=24, block_k=16), 2),  # not a multiple of 16
+    (dict(mask_kind=2, block_mask=16, block_q=64, block_k=16), 2),  # 64 does not divide 96
     (dict(q=None), 1), (dict(lse=None), 1), (dict(dk=None), 1), (dict(dout=None), 1),
     (dict(q=18), 3), (dict(dv=24), 3),
     (dict(ws=None), 4), (dict(ws_bytes=100), 4),

@@ -13,7 +13,8 @@ import torch
 
 import oracle
 from exact_io_aware_attn_amd import attn_bwd, attn_fwd, prepare_bwd
-from exact_io_aware_attn_amd.inputs import WORKLOADS, backward_inputs, workload_inputs
+from exact_io_aware_attn_amd.inputs import (WORKLOADS, backward_inputs, frame_block_mask,
+                                            workload_inputs)
 
 from parity import check_grad, to64
 
@@ -131,3 +132,55 @@ def test_bwd_full_workload_sliced(name, pieces):
         got = (dq[b:b + 1, :, hs], dk[b:b + 1, :, hk:hk + 1], dv[b:b + 1, :, hk:hk + 1])
         errs = [check_grad(g_, r, f"{name} b={b} kv={hk} d{n}") for g_, r, n in zip(got, ref, "QKV")]
         print(name, b, hk, " ".join(f"d{n} {e[0]:.2e}/{e[1]:.2e}" for n, e in zip("QKV", errs)))
+
+
+def _block_mask(nqb, nkb, seed):
+    """Random live blocks (about half), with one block row and one block column
+    left entirely dead."""
+    rng = np.random.default_rng(seed)
+    bm = (rng.random((nqb, nkb)) < 0.5).astype(np.uint8)
+    bm[nqb // 2, :] = 0
+    bm[:, nkb // 3] = 0
+    return bm
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bq,bk", [(16, 16), (32, 48), (48, 16), (80, 80)])
+def test_bwd_block_mask(d, causal, bq, bk):
+    nqb, nkb = max(2, 288 // bq), max(2, 320 // bk)
+    Nq, Nk = nqb * bq, nkb * bk
+    bm = _block_mask(nqb, nkb, seed=bq * 100 + bk + d)
+    q, k, v, do = backward_inputs(2, 4, 2, Nq, Nk, d, torch.bfloat16, seed=bq + bk + d)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = attn_fwd(qd, kd, vd, causal=causal, block_mask=bm, block=(bq, bk))
+    grads = attn_bwd(qd, kd, vd, o, lse, dod, causal=causal, block_mask=bm, block=(bq, bk))
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(to64(q), to64(k), to64(v), to64(do), 1 / math.sqrt(d),
+                                    causal=causal, block_mask=bm, block_q=bq, block_k=bk)
+    where = f"block {bq}x{bk} d={d} c={causal}"
+    errs = [check_grad(g, r, f"{where} d{n}") for g, r, n in zip(grads, ref, "QKV")]
+    print(where, " ".join(f"d{n} {e[0]:.2e}/{e[1]:.2e}" for n, e in zip("QKV", errs)))
+    # rows of the dead block row see no key: exactly zero dQ
+    r0 = (nqb // 2) * bq
+    assert (grads[0][:, r0:r0 + bq].float() == 0).all()
+    # keys of the dead block column are seen by no row: exactly zero dK, dV
+    c0 = (nkb // 3) * bk
+    assert (grads[1][:, c0:c0 + bk].float() == 0).all() and (grads[2][:, c0:c0 + bk].float() == 0).all()
+
+
+def test_bwd_video_workload_one_head():
+    w = WORKLOADS["video-frames-16x880-bwd"]
+    ins = workload_inputs(w, device=DEV)
+    q, k, v, do, bm = ins["q"], ins["k"], ins["v"], ins["dout"], ins["block_mask"]
+    blk = (w.block, w.block)
+    o, lse = attn_fwd(q, k, v, block_mask=bm, block=blk)
+    dq, dk, dv = attn_bwd(q, k, v, o, lse, do, block_mask=bm, block=blk)
+    torch.cuda.synchronize()
+    h = 17
+    ref = oracle.attention_backward(to64(q[:, :, h:h + 1]), to64(k[:, :, h:h + 1]),
+                                    to64(v[:, :, h:h + 1]), to64(do[:, :, h:h + 1]), w.scale,
+                                    block_mask=bm, block_q=w.block, block_k=w.block)
+    got = (dq[:, :, h:h + 1], dk[:, :, h:h + 1], dv[:, :, h:h + 1])
+    errs = [check_grad(g, r, f"video head {h} d{n}") for g, r, n in zip(got, ref, "QKV")]
+    print("video", h, " ".join(f"d{n} {e[0]:.2e}/{e[1]:.2e}" for n, e in zip("QKV", errs)))
