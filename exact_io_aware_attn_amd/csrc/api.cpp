@@ -287,6 +287,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     if (block_q <= 0 || block_k <= 0 || block_q % 16 != 0 || block_k % 16 != 0)
       return MIATTN_ERR_SHAPE;
     if (Nq % block_q != 0 || Nk % block_k != 0) return MIATTN_ERR_SHAPE;
+    // live-tile lists of 64-row tiles per workgroup
+    if ((Nq + 63) / 64 > miattn::kMaxBwdTiles || (Nk + 63) / 64 > miattn::kMaxBwdTiles)
+      return MIATTN_ERR_UNSUPPORTED;
   }
   if (B == 0 || (Nq == 0 && Nk == 0)) return MIATTN_OK;
   if (block && Nq > 0 && Nk > 0 && block_mask == nullptr) return MIATTN_ERR_NULL;

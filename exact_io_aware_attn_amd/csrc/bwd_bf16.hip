@@ -76,6 +76,33 @@ __device__ __forceinline__ bool pair_live(const BwdParams& p, int q, int key) {
   return p.block_mask[(int64_t)(q / p.block_q) * p.nkb + key / p.block_k] != 0;
 }
 
+// Block mask: the streamed tiles (64 rows of queries or keys) that meet a live
+// block of the workgroup's stationary range, compacted in order into list[]
+// by one wave (64 candidate tiles per step); returns their count. The
+// stationary range is block rows [s0, s1] (QSIDE: query blocks, the tiles are
+// key tiles) or block columns [s0, s1] (key blocks, the tiles are query
+// tiles); tile_range(t, a, b) gives the other axis's blocks [a, b] of tile t.
+template <bool QSIDE, typename Range>
+__device__ int live_tiles(const BwdParams& p, int t_begin, int t_end, int s0, int s1, Range tile_range,
+                          short* list, int lane) {
+  int count = 0;
+  for (int base = t_begin; base < t_end; base += 64) {
+    const int t = base + lane;
+    bool live = false;
+    if (t < t_end) {
+      int a, b;
+      tile_range(t, a, b);
+      for (int x = s0; x <= s1 && !live; ++x)
+        for (int y = a; y <= b && !live; ++y)
+          live = (QSIDE ? p.block_mask[(int64_t)x * p.nkb + y] : p.block_mask[(int64_t)y * p.nkb + x]) != 0;
+    }
+    const uint64_t bal = __ballot(live);
+    if (live) list[count + __popcll(bal & ((1ull << lane) - 1ull))] = (short)t;
+    count += __popcll(bal);
+  }
+  return count;
+}
+
 // ---- D_i = dO_i . O_i (fp32) and LSE_i * log2(e), per (batch, head, row);
 // rows Nq .. npad-1 get D = 0 and +inf (their weights exp2(s - inf) are 0).
 // D/8 lanes per row, 16 bytes each.
@@ -127,6 +154,8 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
   __shared__ __attribute__((aligned(16))) __bf16 sQ[2][BT * D];
   __shared__ __attribute__((aligned(16))) __bf16 sG[2][BT * D];    // dO
   __shared__ __attribute__((aligned(16))) float sSt[2][2 * BT];   // lse2 then dsum
+  __shared__ short sTile[BLOCK ? kMaxBwdTiles : 1];  // live query tiles (block mask)
+  __shared__ int sNT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -160,7 +189,25 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
   // queries that can see the workgroup's keys: q >= key - causal_off
   int qb0 = 0;
   if constexpr (CAUSAL) qb0 = max(0, kt * 128 - p.causal_off) / BT * BT;
-  const int n_qt = p.Nq > qb0 ? (p.Nq - qb0 + BT - 1) / BT : 0;
+  int n_qt = p.Nq > qb0 ? (p.Nq - qb0 + BT - 1) / BT : 0;
+  if constexpr (BLOCK) {
+    // query tiles meeting a live block of the workgroup's key blocks
+    if (wave == 0) {
+      const int kb0 = kt * 128 / p.block_k, kb1 = (min(kt * 128 + 128, p.Nk) - 1) / p.block_k;
+      const int n = live_tiles<false>(
+          p, qb0 / BT, (p.Nq + BT - 1) / BT, kb0, kb1,
+          [&](int t, int& a, int& b) {
+            a = t * BT / p.block_q;
+            b = (min(t * BT + BT, p.Nq) - 1) / p.block_q;
+          },
+          sTile, lane);
+      if (lane == 0) sNT = n;
+    }
+    __syncthreads();
+    n_qt = sNT;
+  }
+  // first row of the workgroup's i-th query tile
+  auto tile_row = [&](int i) { return BLOCK ? (int)sTile[i] * BT : qb0 + i * BT; };
   const int n_steps = G * n_qt;  // step s: query head hkv*G + s / n_qt, tile s % n_qt
 
   // ---- staging: instruction j of this wave fills tile rows
@@ -178,7 +225,7 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
   const DmaRsrc rst = dma_rsrc(p.stats, (uint32_t)(2 * nstat * 4));
   auto issue = [&](int st, int buf) {
     const int g = st / n_qt;
-    const int r0 = qb0 + (st - g * n_qt) * BT;
+    const int r0 = tile_row(st - g * n_qt);
     const int hq = hkv * G + g;
     const int nvalid = min(BT, p.Nq - r0);
     const __bf16* qb = (const __bf16*)p.q + b * p.q_sb + (int64_t)r0 * p.q_ss + hq * p.q_sh;
@@ -376,7 +423,7 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
 
   auto body = [&](int st, int buf) {
     const int g = st / n_qt;
-    const int r0 = qb0 + (st - g * n_qt) * BT;
+    const int r0 = tile_row(st - g * n_qt);
     const __bf16* sq = sQ[buf];
     const __bf16* sg = sG[buf];
     const float* ss = sSt[buf];
@@ -456,6 +503,8 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
 
   __shared__ __attribute__((aligned(16))) __bf16 sK[2][BT * D];  // vswz (read both ways)
   __shared__ __attribute__((aligned(16))) __bf16 sV[2][BT * D];  // kswz (read as rows)
+  __shared__ short sTile[BLOCK ? kMaxBwdTiles : 1];  // live key tiles (block mask)
+  __shared__ int sNT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -495,7 +544,24 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
   int kv_end = p.Nk;
   if constexpr (CAUSAL)
     kv_end = min(p.Nk, max(0, min(qt * 128 + 127, p.Nq - 1) + p.causal_off + 1));
-  const int n_tiles = (kv_end + BT - 1) / BT;
+  int n_tiles = (kv_end + BT - 1) / BT;
+  if constexpr (BLOCK) {
+    // key tiles meeting a live block of the workgroup's block rows
+    if (wave == 0) {
+      const int r_lo = qt * 128, r_hi = min(qt * 128 + 128, p.Nq) - 1;
+      const int n = live_tiles<true>(
+          p, 0, n_tiles, r_lo / p.block_q, r_hi / p.block_q,
+          [&](int t, int& a, int& b) {
+            a = t * BT / p.block_k;
+            b = (min(t * BT + BT, kv_end) - 1) / p.block_k;
+          },
+          sTile, lane);
+      if (lane == 0) sNT = n;
+    }
+    __syncthreads();
+    n_tiles = sNT;
+  }
+  auto tile_of = [&](int i) { return BLOCK ? (int)sTile[i] : i; };
 
   const __bf16* kg = (const __bf16*)p.k + b * p.k_sb + hkv * p.k_sh;
   const __bf16* vg = (const __bf16*)p.v + b * p.v_sb + hkv * p.v_sh;
@@ -675,13 +741,13 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
     }
   };
 
-  if (n_tiles > 0) issue(0, 0);
+  if (n_tiles > 0) issue(tile_of(0), 0);
   wait_all_loads();
   __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) issue(t + 1, buf ^ 1);
-    body(t, buf);
+  for (int i = 0; i < n_tiles; ++i) {
+    const int buf = i & 1;
+    if (i + 1 < n_tiles) issue(tile_of(i + 1), buf ^ 1);
+    body(tile_of(i), buf);
     wait_all_loads();
     __syncthreads();
   }

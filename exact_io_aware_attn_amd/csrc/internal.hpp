@@ -105,6 +105,8 @@ struct BwdParams {
 };
 
 constexpr int kMaxSplits = 4096;
+// backward with a block mask: at most this many 64-row tiles per side
+constexpr int kMaxBwdTiles = 4096;
 int decode_waves_per_group(int Hkv);
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, bool block,
