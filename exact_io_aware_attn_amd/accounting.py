@@ -79,7 +79,10 @@ def workload_work(w, block_mask=None, seqlens=None):
     """(flops, bytes) of one call of a named workload."""
     eb = 2 if w.dtype == "bf16" else 4
     if w.kind == "decode":
-        return decode_flops(seqlens, w.Hq, w.d), decode_kv_bytes(seqlens, w.Hkv, w.d, eb)
+        # several new tokens share one read of the cache (their FLOPs: about 4 d
+        # per token and cached row)
+        return (decode_flops(seqlens, w.Hq, w.d) * w.n_new,
+                decode_kv_bytes(seqlens, w.Hkv, w.d, eb))
     pairs = attended_pairs(w.Nq, w.Nk, causal=w.causal, block_mask=block_mask,
                            block_q=w.block or None, block_k=w.block or None)
     if w.kind == "backward":

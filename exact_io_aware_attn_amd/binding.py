@@ -22,7 +22,8 @@ MIATTN_MASK_NONE, MIATTN_MASK_CAUSAL, MIATTN_MASK_BLOCK = 0, 1, 2
 SOFTMAX_MODES = {"online": 0, "fixed_max": 1, "fixed_max_centered": 2}
 
 _EXPORTS = ("attn_fwd", "attn_fwd_workspace_bytes", "attn_decode",
-            "attn_decode_workspace_bytes", "attn_bwd", "attn_bwd_workspace_bytes",
+            "attn_decode_workspace_bytes", "attn_decode_multi",
+            "attn_decode_multi_workspace_bytes", "attn_bwd", "attn_bwd_workspace_bytes",
             "attn_status_str")
 
 
@@ -60,6 +61,11 @@ def library():
     lib.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I,
                                 ctypes.POINTER(_Strides), P, Z, P]
     lib.attn_decode.restype = I
+    lib.attn_decode_multi_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.attn_decode_multi_workspace_bytes.restype = Z
+    lib.attn_decode_multi.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I,
+                                      ctypes.POINTER(_Strides), P, Z, P]
+    lib.attn_decode_multi.restype = I
     lib.attn_bwd_workspace_bytes.argtypes = [I, I, I]
     lib.attn_bwd_workspace_bytes.restype = Z
     lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, I, I,
@@ -80,6 +86,11 @@ def attn_fwd_workspace_bytes(B, Hkv, Nq, Nk, d, mask_kind, block_q, softmax_mode
 
 def attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d, kv_splits=0):
     return int(library().attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d, kv_splits))
+
+
+def attn_decode_multi_workspace_bytes(B, n_new, Hq, Hkv, max_len, d, kv_splits=0):
+    return int(library().attn_decode_multi_workspace_bytes(B, n_new, Hq, Hkv, max_len, d,
+                                                           kv_splits))
 
 
 def attn_bwd_workspace_bytes(B, Hq, Nq):
@@ -296,3 +307,51 @@ def prepare_bwd(q, k, v, o, lse, dout, *, causal=False, block_mask=None, block=N
     args, grads, keep = _bwd_setup(q, k, v, o, lse, dout, causal, block_mask, block, scale, dq,
                                    dk, dv, workspace)
     return PreparedCall(library().attn_bwd, args, "attn_bwd", keep), grads
+
+
+def _decode_multi_setup(q, k_cache, v_cache, seqlens, scale, kv_splits, return_lse, out,
+                        lse_out, workspace):
+    _check_gpu(q, k_cache, v_cache, seqlens)
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B,n_new,Hq,d]; caches [B,max_len,Hkv,d]")
+    if seqlens.dtype != torch.int32:
+        raise TypeError("seqlens must be int32")
+    B, nt, Hq, d = q.shape
+    _, max_len, Hkv, _ = k_cache.shape
+    dev = q.device
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    q = q.contiguous()
+    seqlens = seqlens.contiguous()
+    o = torch.empty_like(q) if out is None else out
+    lse = None
+    if return_lse:
+        lse = torch.empty((B, nt, Hq), dtype=torch.float32, device=dev) if lse_out is None else lse_out
+    need = attn_decode_multi_workspace_bytes(B, nt, Hq, Hkv, max_len, d, kv_splits)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = (_Strides * 2)(_strides4(k_cache), _strides4(v_cache))
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse),
+            _dtype_code(q), B, nt, Hq, Hkv, max_len, d, scale, kv_splits, st, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(dev))
+    return args, o, lse, (q, k_cache, v_cache, seqlens, o, lse, workspace, st)
+
+
+def attn_decode_multi(q, k_cache, v_cache, seqlens, *, scale=None, kv_splits=0, return_lse=True,
+                      out=None, lse_out=None, workspace=None):
+    """Decode of n_new tokens per sequence: q [B,n_new,Hq,d] bf16 against caches
+    [B,max_len,Hkv,d] whose last seqlens[b] rows include the new tokens' own keys.
+    Returns (o [B,n_new,Hq,d], lse [B,n_new,Hq] or None)."""
+    args, o, lse, _ = _decode_multi_setup(q, k_cache, v_cache, seqlens, scale, kv_splits,
+                                          return_lse, out, lse_out, workspace)
+    rc = library().attn_decode_multi(*args)
+    if rc != 0:
+        raise MiattnError(rc, "attn_decode_multi")
+    return o, lse
+
+
+def prepare_decode_multi(q, k_cache, v_cache, seqlens, *, scale=None, kv_splits=0,
+                         return_lse=True, out=None, lse_out=None, workspace=None):
+    """attn_decode_multi as a PreparedCall: returns (call, o, lse)."""
+    args, o, lse, keep = _decode_multi_setup(q, k_cache, v_cache, seqlens, scale, kv_splits,
+                                             return_lse, out, lse_out, workspace)
+    return PreparedCall(library().attn_decode_multi, args, "attn_decode_multi", keep), o, lse

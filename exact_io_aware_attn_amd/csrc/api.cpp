@@ -218,16 +218,28 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d, i
   return decode_ws(B, Hq, d);
 }
 
-int attn_decode(const void* q, const void* k_cache, const void* v_cache,
-                const int32_t* seqlens, void* o, float* lse, int dtype, int B, int Hq, int Hkv,
-                int max_len, int d, float scale, int kv_splits,
+size_t attn_decode_multi_workspace_bytes(int B, int n_new, int Hq, int Hkv, int max_len, int d,
+                                         int kv_splits) {
+  (void)max_len;
+  (void)kv_splits;
+  if (B <= 0 || n_new <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return 0;
+  return decode_ws(B, Hq * n_new, d);
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_impl(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* seqlens, void* o, float* lse, int dtype, int B, int nt, int Hq,
+                int Hkv, int max_len, int d, float scale, int kv_splits,
                 const miattn_strides* cache_strides, void* workspace, size_t workspace_bytes,
                 void* stream) {
   if (dtype != MIATTN_BF16) return MIATTN_ERR_UNSUPPORTED;
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || max_len < 0 || d <= 0) return MIATTN_ERR_SHAPE;
+  if (B < 0 || nt <= 0 || Hq <= 0 || Hkv <= 0 || max_len < 0 || d <= 0) return MIATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return MIATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return MIATTN_ERR_UNSUPPORTED;
-  if (Hq / Hkv > 16) return MIATTN_ERR_UNSUPPORTED;
+  if ((Hq / Hkv) * nt > 16) return MIATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(scale) || !(scale > 0.f)) return MIATTN_ERR_ARG;
   if (kv_splits < 0 || kv_splits > miattn::kMaxSplits) return MIATTN_ERR_ARG;
   if (B == 0) return MIATTN_OK;
@@ -247,21 +259,43 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
     return MIATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return MIATTN_ERR_UNSUPPORTED;
 
-  const size_t need = decode_ws(B, Hq, d);
-  const size_t po = align_up((size_t)(miattn::kMaxSplits + B) * Hq * d * sizeof(float));
+  const size_t need = decode_ws(B, Hq * nt, d);
+  const size_t po = align_up((size_t)(miattn::kMaxSplits + B) * Hq * nt * d * sizeof(float));
   if (workspace == nullptr || workspace_bytes < need) return MIATTN_ERR_WORKSPACE;
 
   miattn::DecodeParams p{};
   p.q = q; p.kc = k_cache; p.vc = v_cache; p.seqlens = seqlens; p.o = o; p.lse = lse;
   p.k_sb = sk.b; p.k_ss = sk.s; p.k_sh = sk.h;
   p.v_sb = sv.b; p.v_ss = sv.s; p.v_sh = sv.h;
-  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.max_len = max_len;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.max_len = max_len; p.nt = nt;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.n_splits = decode_splits(Hkv, kv_splits);
   p.part_o = (float*)workspace;
   p.part_lse = (float*)((char*)workspace + po);
   hipError_t e = miattn::launch_decode(p, d, (hipStream_t)stream);
   return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* seqlens, void* o, float* lse, int dtype, int B, int Hq, int Hkv,
+                int max_len, int d, float scale, int kv_splits,
+                const miattn_strides* cache_strides, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  return decode_impl(q, k_cache, v_cache, seqlens, o, lse, dtype, B, 1, Hq, Hkv, max_len, d, scale,
+                     kv_splits, cache_strides, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seqlens, void* o, float* lse, int dtype, int B, int n_new,
+                      int Hq, int Hkv, int max_len, int d, float scale, int kv_splits,
+                      const miattn_strides* cache_strides, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_cache, v_cache, seqlens, o, lse, dtype, B, n_new, Hq, Hkv, max_len, d,
+                     scale, kv_splits, cache_strides, workspace, workspace_bytes, stream);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq) {

@@ -1,5 +1,6 @@
-// Decode attention: one new query token per sequence against a KV cache,
-// split over the cache ("split-K") and merged with the block rule.
+// Decode attention: one new query token per sequence (or nt <= 16/G new
+// tokens, causal among themselves) against a KV cache, split over the cache
+// ("split-K") and merged with the block rule.
 //
 // Decode reads every cached key and value once per generated token and does
 // O(1) FLOPs per byte, so it is bound by HBM bandwidth ("Attention Mechanism
@@ -24,7 +25,11 @@
 //    flight while the current one is consumed, and no workgroup barrier sits
 //    in the key loop;
 //  * S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16 with the
-//    query heads of the group as the 16-wide N dimension (zero-padded);
+//    query rows of the group -- nt new tokens x G query heads, row t*G + g --
+//    as the 16-wide N dimension (zero-padded). The new tokens' own keys are
+//    the last nt cached rows: token t sees cache rows below len - nt + t + 1
+//    (the causal rule aligned at the end), so several tokens verified or
+//    generated at once share one read of the cache;
 //  * rows at or past seqlens[b] are never read;
 //  * partial (range i, sequence b) is stored in slot i + b: the (i, b) pairs
 //    that meet form a monotone staircase, so i + b is unique. A second kernel
@@ -77,7 +82,7 @@ __global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) decode_split_ke
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int n = lane & 15;    // query head (column) of this lane
+  const int n = lane & 15;    // query row (column) of this lane: token n / G, head n % G
   const int g4 = lane >> 4;   // lane group
   const int hkv = blockIdx.y * NW + wave;
   const int G = p.Hq / p.Hkv;
@@ -113,12 +118,16 @@ __global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) decode_split_ke
       const __bf16* kg = kbase + b * p.k_sb + lch * 8;
       const __bf16* vg = vbase + b * p.v_sb + lch * 8;
 
-      // Q^T as B operand: lane (n, g4), k-step t holds q[head n][32t + 8g4 .. +8]
+      // Q^T as B operand: lane (n, g4), k-step t holds q[row n][32t + 8g4 .. +8]
+      const int tok = n / G, hg = n - tok * G;
+      // keys this row may see: cache rows below len - nt + tok + 1
+      const int k_lim = len - p.nt + tok + 1;
       bf16x8 qf[KST];
       {
-        const bool ok = n < G;
-        const __bf16* qp =
-            (const __bf16*)p.q + ((int64_t)b * p.Hq + hkv * G + (ok ? n : 0)) * D + 8 * g4;
+        const bool ok = n < G * p.nt;
+        const __bf16* qp = (const __bf16*)p.q +
+                           (((int64_t)b * p.nt + (ok ? tok : 0)) * p.Hq + hkv * G + (ok ? hg : 0)) * D +
+                           8 * g4;
 #pragma unroll
         for (int t = 0; t < KST; ++t) {
           bf16x8 z = {};
@@ -182,7 +191,7 @@ __global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) decode_split_ke
           for (int r = 0; r < 4; ++r) {
             const int key = s0 + 16 * mb2 + 4 * g4 + r;
             float x = s[mb2][r] * p.scale_log2;
-            if (key >= k_end) x = kNegInf;
+            if (key >= k_end || key >= k_lim) x = kNegInf;
             s[mb2][r] = x;
             mx = fmaxf(mx, x);
           }
@@ -230,8 +239,8 @@ __global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) decode_split_ke
       float l_tot = l_run;
       l_tot += shfl_xor(l_tot, 16);
       l_tot += shfl_xor(l_tot, 32);
-      if (n < G) {
-        const int64_t row = (wg + b) * p.Hq + hkv * G + n;
+      if (n < G * p.nt) {
+        const int64_t row = ((wg + b) * p.nt + tok) * p.Hq + hkv * G + hg;
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         float* po = p.part_o + row * D + 4 * g4;
 #pragma unroll
@@ -243,13 +252,14 @@ __global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) decode_split_ke
   }
 }
 
-// One workgroup (a single wave) per (batch, query head): merge the partials
-// of the ranges that met the sequence. Each lane owns d / 64 columns.
+// One workgroup (a single wave) per (batch, new token, query head): merge the
+// partials of the ranges that met the sequence. Each lane owns d / 64 columns.
 template <int D>
 __global__ void __launch_bounds__(64) decode_merge_kernel(const DecodeParams p) {
   constexpr int PER = D / 64;
-  const int bh = blockIdx.x;
-  const int b = bh / p.Hq, hq = bh - b * p.Hq;
+  const int bh = blockIdx.x;  // (b * nt + token) * Hq + hq
+  const int rows = p.nt * p.Hq;
+  const int b = bh / rows, th = bh - b * rows;
   const int lane = threadIdx.x;
   const int64_t T = wave_sum_lens(p.seqlens, p.B, lane);
   const int64_t start = wave_sum_lens(p.seqlens, b, lane);
@@ -261,10 +271,10 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(const DecodeParams p) 
   if (len > 0) {
     const int64_t S = p.n_splits < T ? p.n_splits : T;
     const int64_t i0 = owner(start, T, S), i1 = owner(start + len - 1, T, S);
-    for (int64_t i = i0; i <= i1; ++i) M = fmaxf(M, p.part_lse[(i + b) * p.Hq + hq]);
+    for (int64_t i = i0; i <= i1; ++i) M = fmaxf(M, p.part_lse[(i + b) * rows + th]);
     const float Mu = M == kNegInf ? 0.f : M;
     for (int64_t i = i0; i <= i1; ++i) {
-      const int64_t row = (i + b) * p.Hq + hq;
+      const int64_t row = (i + b) * rows + th;
       const float w = __expf(p.part_lse[row] - Mu);
       W += w;
 #pragma unroll
@@ -303,9 +313,9 @@ hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (d == 64)
-    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(p.B * p.Hq), dim3(64), 0, s, p);
+    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(p.B * p.nt * p.Hq), dim3(64), 0, s, p);
   else
-    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(p.B * p.Hq), dim3(64), 0, s, p);
+    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(p.B * p.nt * p.Hq), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -68,10 +68,11 @@ struct DecodeParams {
   int64_t k_sb, k_ss, k_sh;
   int64_t v_sb, v_ss, v_sh;
   int B, Hq, Hkv, max_len;
+  int nt;            // new tokens per sequence (rows of q per sequence), nt * Hq/Hkv <= 16
   float scale_log2;
   int n_splits;      // ranges the flattened cache is cut into (<= kMaxSplits)
-  float* part_o;     // [n_splits + B][Hq][d], slot = range + batch
-  float* part_lse;   // [n_splits + B][Hq]
+  float* part_o;     // [n_splits + B][nt][Hq][d], slot = range + batch
+  float* part_lse;   // [n_splits + B][nt][Hq]
 };
 
 // Backward pass (bf16). The statistics live in the caller's workspace, one

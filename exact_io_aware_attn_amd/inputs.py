@@ -35,6 +35,7 @@ class Workload:
     len_lo: int = 0           # decode key lengths, uniform in [len_lo, len_hi]
     len_hi: int = 0
     softmax: tuple = field(default=("online",))
+    n_new: int = 1            # decode: new tokens per sequence (causal among themselves)
 
     @property
     def scale(self):
@@ -65,6 +66,11 @@ WORKLOADS = {
     "llama3-8b-gqa-causal-8k-bwd": Workload("llama3-8b-gqa-causal-8k-bwd", "backward", B=1,
                                             Hq=32, Hkv=8, Nq=8192, Nk=8192, d=128,
                                             dtype="bf16", causal=True, seed=7),
+    # decode of 4 new tokens per sequence at once (4 tokens x 4 query heads fill the
+    # 16 query rows a KV head's products carry)
+    "gqa-decode-b64-4tok": Workload("gqa-decode-b64-4tok", "decode", B=64, Hq=32, Hkv=8, Nq=4,
+                                    Nk=32768, d=128, dtype="bf16", seed=10, len_lo=1024,
+                                    len_hi=32768, n_new=4),
     "gpt2-medium-causal-bwd": Workload("gpt2-medium-causal-bwd", "backward", B=64, Hq=16,
                                        Hkv=16, Nq=1024, Nk=1024, d=64, dtype="bf16",
                                        causal=True, seed=8),
@@ -129,6 +135,20 @@ def decode_inputs(B, Hq, Hkv, max_len, d, dtype=torch.bfloat16, seed=0, len_lo=1
     return seqlens, q, kc, vc
 
 
+def decode_multi_inputs(B, n_new, Hq, Hkv, max_len, d, dtype=torch.bfloat16, seed=0, len_lo=1,
+                        len_hi=None, device="cpu"):
+    """As decode_inputs, with q [B, n_new, Hq, d] (the new tokens, whose own keys
+    are the last n_new cached rows of each sequence)."""
+    len_hi = max_len if len_hi is None else len_hi
+    g = _gen(device, seed)
+    seqlens = torch.randint(len_lo, len_hi + 1, (B,), generator=g, device=device,
+                            dtype=torch.int64).to(torch.int32)
+    q = _randn((B, n_new, Hq, d), g, device, dtype)
+    kc = _randn((B, max_len, Hkv, d), g, device, dtype)
+    vc = _randn((B, max_len, Hkv, d), g, device, dtype)
+    return seqlens, q, kc, vc
+
+
 def frame_block_mask(frames, frame_len, block, window=1, ref_frame=0):
     """uint8 [n, n] block mask, n = frames * frame_len / block.
 
@@ -164,6 +184,10 @@ def workload_inputs(w: Workload, device="cpu"):
         if w.frames:
             out["block_mask"] = frame_block_mask(w.frames, w.frame_len, w.block)
         return out
-    seqlens, q, kc, vc = decode_inputs(w.B, w.Hq, w.Hkv, w.Nk, w.d, w.torch_dtype,
-                                       w.seed, w.len_lo, w.len_hi, device)
+    if w.n_new > 1:
+        seqlens, q, kc, vc = decode_multi_inputs(w.B, w.n_new, w.Hq, w.Hkv, w.Nk, w.d,
+                                                 w.torch_dtype, w.seed, w.len_lo, w.len_hi, device)
+    else:
+        seqlens, q, kc, vc = decode_inputs(w.B, w.Hq, w.Hkv, w.Nk, w.d, w.torch_dtype,
+                                           w.seed, w.len_lo, w.len_hi, device)
     return dict(seqlens=seqlens, q=q, k_cache=kc, v_cache=vc)

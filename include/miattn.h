@@ -155,6 +155,34 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 const miattn_strides* cache_strides, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace attn_decode_multi needs (0 when the sizes are
+ * invalid). Independent of max_len and kv_splits. */
+size_t attn_decode_multi_workspace_bytes(int B, int n_new, int Hq, int Hkv, int max_len, int d,
+                                         int kv_splits);
+
+/* Decode of several new tokens per sequence at once (for example the draft
+ * tokens of speculative or multi-token decoding): n_new query rows per
+ * sequence whose own keys and values are already the last n_new cached rows,
+ * causal among themselves. Row t (0-based) of sequence b attends to cached
+ * rows 0 .. seqlens[b] - n_new + t -- the causal rule of attn_fwd with the
+ * rows aligned at the end ("Two Phases of Inference", Decode, one token at a
+ * time; the same rule for several). All rows of a sequence share one read of
+ * the cache: the n_new x (Hq/Hkv) rows of a KV head fill the 16-wide side of
+ * the matrix products. Same split-K and merge as attn_decode.
+ *
+ * q        device, [B, n_new, Hq, d] bf16, packed  (read)
+ * o        device, [B, n_new, Hq, d] bf16, packed  (written)
+ * lse      device, float [B, n_new, Hq] or NULL     (written)
+ * n_new    >= 1 with n_new * (Hq / Hkv) <= 16
+ * other arguments as in attn_decode; workspace at least
+ * attn_decode_multi_workspace_bytes(...) bytes. A row that sees no cached row
+ * (seqlens[b] - n_new + t < 0) yields O = 0 and LSE = -inf. */
+int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seqlens, void* o, float* lse, int dtype, int B, int n_new,
+                      int Hq, int Hkv, int max_len, int d, float scale, int kv_splits,
+                      const miattn_strides* cache_strides, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace attn_bwd needs: two fp32 rows of Nq rounded up
  * to 64 per (batch, query head) -- the forward LSE in base-2 units and
  * D_i = dO_i . O_i. Returns 0 for invalid sizes. */

@@ -152,3 +152,31 @@ def _bwd(**kw):
 def test_bwd_validation(kw, status):
     """Each of these returns before anything is enqueued (no GPU needed)."""
     assert _bwd(**kw) == status
+
+
+def _decm(**kw):
+    a = dict(q=16, k=16, v=16, seqlens=16, o=16, lse=None, dtype=0, B=2, nt=4, Hq=8, Hkv=2,
+             max_len=256, d=128, scale=0.1, chunk=0, ws=None, ws_bytes=0)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return bd.library().attn_decode_multi(P(a["q"]), P(a["k"]), P(a["v"]), P(a["seqlens"]),
+                                          P(a["o"]), P(a["lse"]), a["dtype"], a["B"], a["nt"],
+                                          a["Hq"], a["Hkv"], a["max_len"], a["d"], a["scale"],
+                                          a["chunk"], None, P(a["ws"]), a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nt=0), 2), (dict(nt=5), 3),            # 5 tokens x 4 heads > 16 rows
+    (dict(nt=16, Hq=2, Hkv=2), 4),               # 16 x 1 fits; workspace missing
+    (dict(dtype=1), 3), (dict(d=80), 3), (dict(Hq=7), 2), (dict(scale=-1.0), 6),
+    (dict(seqlens=None), 1), (dict(ws=None), 4), (dict(B=0), 0),
+])
+def test_decode_multi_validation(kw, status):
+    assert _decm(**kw) == status
+
+
+def test_decode_multi_workspace_scales_with_tokens():
+    one = bd.attn_decode_workspace_bytes(64, 32, 8, 32768, 128, 0)
+    assert bd.attn_decode_multi_workspace_bytes(64, 1, 32, 8, 32768, 128, 0) == one
+    assert bd.attn_decode_multi_workspace_bytes(64, 4, 32, 8, 32768, 128, 0) >= 4 * one - 4096
+    assert bd.attn_decode_multi_workspace_bytes(64, 0, 32, 8, 32768, 128, 0) == 0

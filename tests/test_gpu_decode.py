@@ -7,8 +7,8 @@ import pytest
 import torch
 
 import oracle
-from exact_io_aware_attn_amd import attn_decode
-from exact_io_aware_attn_amd.inputs import WORKLOADS, decode_inputs
+from exact_io_aware_attn_amd import attn_decode, attn_decode_multi
+from exact_io_aware_attn_amd.inputs import WORKLOADS, decode_inputs, decode_multi_inputs
 
 from parity import check, to64
 
@@ -112,3 +112,56 @@ def test_full_gqa_decode_b64():
         O, L = oracle.decode(to64(q[b:b + 1]), to64(kc[b:b + 1, :n]), to64(vc[b:b + 1, :n]),
                              np.array([n]), w.scale)
         check(o[b:b + 1], O, lse[b:b + 1], L, where=f"full decode b={b} len={n}")
+
+
+# ------------------------------------------------------------ several new tokens
+def _multi_ref(q, kc, vc, seqlens, scale):
+    """Per sequence: the new tokens' rows against its first seqlens[b] cached rows,
+    causal with the rows aligned at the end (the oracle's prefill rule)."""
+    B, nt, Hq, d = q.shape
+    O = np.zeros((B, nt, Hq, d))
+    L = np.full((B, nt, Hq), -np.inf)
+    for b in range(B):
+        n = int(seqlens[b])
+        if n == 0:
+            continue
+        Ob, Lb = oracle.attention(to64(q[b:b + 1]), to64(kc[b:b + 1, :n]), to64(vc[b:b + 1, :n]),
+                                  scale, causal=True)
+        O[b] = Ob[0]
+        L[b] = Lb[0].T
+    return O, L
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("nt,Hq,Hkv", [(2, 8, 2), (3, 8, 2), (4, 8, 2), (16, 2, 2), (2, 16, 2)])
+@pytest.mark.parametrize("kv_splits", [0, 1, 7])
+def test_decode_multi_tokens(d, nt, Hq, Hkv, kv_splits):
+    seqlens, q, kc, vc = decode_multi_inputs(5, nt, Hq, Hkv, 700, d, seed=nt * 10 + d, len_lo=1)
+    seqlens[0] = 0                     # empty sequence
+    seqlens[1] = max(1, nt - 1)        # fewer cached rows than new tokens: the first rows see none
+    o, lse = attn_decode_multi(q.to(DEV), kc.to(DEV), vc.to(DEV), seqlens.to(DEV), kv_splits=kv_splits)
+    torch.cuda.synchronize()
+    O, L = _multi_ref(q, kc, vc, seqlens.numpy(), 1 / math.sqrt(d))
+    check(o, O, lse, L, where=f"multi nt={nt} H={Hq}/{Hkv} d={d} splits={kv_splits}")
+
+
+def test_decode_multi_one_token_equals_decode():
+    seqlens, q, kc, vc = decode_inputs(6, 32, 8, 900, 128, seed=12, len_lo=0)
+    args = (kc.to(DEV), vc.to(DEV), seqlens.to(DEV))
+    o1, l1 = attn_decode(q.to(DEV), *args)
+    o2, l2 = attn_decode_multi(q[:, None].contiguous().to(DEV), *args)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2[:, 0]) and torch.equal(l1, l2[:, 0])
+
+
+def test_full_gqa_decode_b64_4tok_sampled():
+    w = WORKLOADS["gqa-decode-b64-4tok"]
+    from exact_io_aware_attn_amd.inputs import workload_inputs
+    ins = workload_inputs(w, device=DEV)
+    o, lse = attn_decode_multi(ins["q"], ins["k_cache"], ins["v_cache"], ins["seqlens"])
+    torch.cuda.synchronize()
+    sl = ins["seqlens"].cpu()
+    for b in (0, 17, 63):
+        O, L = _multi_ref(ins["q"][b:b + 1].cpu(), ins["k_cache"][b:b + 1].cpu(),
+                          ins["v_cache"][b:b + 1].cpu(), sl[b:b + 1].numpy(), w.scale)
+        check(o[b:b + 1], O, lse[b:b + 1], L, where=f"gqa-decode-b64-4tok b={b}")

@@ -52,7 +52,8 @@ def test_named_workloads():
     assert set(WORKLOADS) == {"tiny-f32", "gpt2-causal", "llama3-8b-gqa-causal-8k",
                               "gqa-decode-b64", "video-frames-16x880",
                               "gpt2-medium-causal", "llama3-8b-gqa-causal-8k-bwd",
-                              "gpt2-medium-causal-bwd", "video-frames-16x880-bwd"}
+                              "gpt2-medium-causal-bwd", "video-frames-16x880-bwd",
+                              "gqa-decode-b64-4tok"}
     assert WORKLOADS["llama3-8b-gqa-causal-8k"].scale == 1 / 128 ** 0.5
 
 
