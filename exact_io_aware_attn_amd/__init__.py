@@ -7,7 +7,8 @@ inputs and the work accounting used by the tests and the benchmark.
 from . import accounting, inputs  # noqa: F401
 
 _BINDING_NAMES = ("attn_fwd", "attn_decode", "attn_decode_multi", "attn_bwd", "prepare_fwd",
-                  "prepare_decode", "prepare_decode_multi", "prepare_bwd",
+                  "prepare_decode", "prepare_decode_multi", "prepare_bwd", "attn_decode_paged",
+                  "prepare_decode_paged",
                   "attn_decode_multi_workspace_bytes", "attn_fwd_workspace_bytes", "attn_decode_workspace_bytes",
                   "attn_bwd_workspace_bytes",
                   "attn_status_str", "library", "MiattnError")

@@ -23,7 +23,8 @@ SOFTMAX_MODES = {"online": 0, "fixed_max": 1, "fixed_max_centered": 2}
 
 _EXPORTS = ("attn_fwd", "attn_fwd_workspace_bytes", "attn_decode",
             "attn_decode_workspace_bytes", "attn_decode_multi",
-            "attn_decode_multi_workspace_bytes", "attn_bwd", "attn_bwd_workspace_bytes",
+            "attn_decode_multi_workspace_bytes", "attn_decode_paged", "attn_bwd",
+            "attn_bwd_workspace_bytes",
             "attn_status_str")
 
 
@@ -66,6 +67,9 @@ def library():
     lib.attn_decode_multi.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I,
                                       ctypes.POINTER(_Strides), P, Z, P]
     lib.attn_decode_multi.restype = I
+    lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I,
+                                      ctypes.POINTER(_Strides), P, Z, P]
+    lib.attn_decode_paged.restype = I
     lib.attn_bwd_workspace_bytes.argtypes = [I, I, I]
     lib.attn_bwd_workspace_bytes.restype = Z
     lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, I, I,
@@ -355,3 +359,57 @@ def prepare_decode_multi(q, k_cache, v_cache, seqlens, *, scale=None, kv_splits=
     args, o, lse, keep = _decode_multi_setup(q, k_cache, v_cache, seqlens, scale, kv_splits,
                                              return_lse, out, lse_out, workspace)
     return PreparedCall(library().attn_decode_multi, args, "attn_decode_multi", keep), o, lse
+
+
+def _decode_paged_setup(q, k_pages, v_pages, block_table, seqlens, scale, kv_splits, return_lse,
+                        out, lse_out, workspace):
+    _check_gpu(q, k_pages, v_pages, block_table, seqlens)
+    if q.dim() == 3:
+        q = q[:, None]
+    if q.dim() != 4 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
+        raise ValueError("q must be [B,n_new,Hq,d] (or [B,Hq,d]); pages [num_pages,page_size,Hkv,d]")
+    if seqlens.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise TypeError("seqlens and block_table must be int32")
+    B, nt, Hq, d = q.shape
+    _, page_size, Hkv, _ = k_pages.shape
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    max_pages = block_table.shape[1]
+    dev = q.device
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    q = q.contiguous()
+    seqlens = seqlens.contiguous()
+    block_table = block_table.contiguous()
+    o = torch.empty_like(q) if out is None else out
+    lse = None
+    if return_lse:
+        lse = torch.empty((B, nt, Hq), dtype=torch.float32, device=dev) if lse_out is None else lse_out
+    need = attn_decode_multi_workspace_bytes(B, nt, Hq, Hkv, page_size * max_pages, d, kv_splits)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = (_Strides * 2)(_strides4(k_pages), _strides4(v_pages))
+    args = (_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seqlens), _ptr(o),
+            _ptr(lse), _dtype_code(q), B, nt, Hq, Hkv, page_size, max_pages, d, scale, kv_splits,
+            st, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    return args, o, lse, (q, k_pages, v_pages, block_table, seqlens, o, lse, workspace, st)
+
+
+def attn_decode_paged(q, k_pages, v_pages, block_table, seqlens, *, scale=None, kv_splits=0,
+                      return_lse=True, out=None, lse_out=None, workspace=None):
+    """Decode against a paged cache: q [B,n_new,Hq,d] (or [B,Hq,d]) bf16, pages
+    [num_pages,page_size,Hkv,d] bf16, block_table int32 [B,max_pages], seqlens int32
+    [B]. Returns (o [B,n_new,Hq,d], lse [B,n_new,Hq] or None)."""
+    args, o, lse, _ = _decode_paged_setup(q, k_pages, v_pages, block_table, seqlens, scale,
+                                          kv_splits, return_lse, out, lse_out, workspace)
+    rc = library().attn_decode_paged(*args)
+    if rc != 0:
+        raise MiattnError(rc, "attn_decode_paged")
+    return o, lse
+
+
+def prepare_decode_paged(q, k_pages, v_pages, block_table, seqlens, *, scale=None, kv_splits=0,
+                         return_lse=True, out=None, lse_out=None, workspace=None):
+    """attn_decode_paged as a PreparedCall: returns (call, o, lse)."""
+    args, o, lse, keep = _decode_paged_setup(q, k_pages, v_pages, block_table, seqlens, scale,
+                                             kv_splits, return_lse, out, lse_out, workspace)
+    return PreparedCall(library().attn_decode_paged, args, "attn_decode_paged", keep), o, lse

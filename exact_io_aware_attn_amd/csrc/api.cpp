@@ -234,7 +234,8 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* seqlens, void* o, float* lse, int dtype, int B, int nt, int Hq,
                 int Hkv, int max_len, int d, float scale, int kv_splits,
                 const miattn_strides* cache_strides, void* workspace, size_t workspace_bytes,
-                void* stream) {
+                void* stream, const int32_t* table = nullptr, int page_size = 0,
+                int max_pages = 0) {
   if (dtype != MIATTN_BF16) return MIATTN_ERR_UNSUPPORTED;
   if (B < 0 || nt <= 0 || Hq <= 0 || Hkv <= 0 || max_len < 0 || d <= 0) return MIATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return MIATTN_ERR_SHAPE;
@@ -246,16 +247,20 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   if (q == nullptr || o == nullptr || seqlens == nullptr) return MIATTN_ERR_NULL;
   if (max_len > 0 && (k_cache == nullptr || v_cache == nullptr)) return MIATTN_ERR_NULL;
 
-  miattn_strides sk{(int64_t)max_len * Hkv * d, (int64_t)Hkv * d, d};
+  const bool paged = table != nullptr;
+  // paged: "b" strides step from page to page, max_len rows fit one page
+  const int rows = paged ? page_size : max_len;
+  miattn_strides sk{(int64_t)rows * Hkv * d, (int64_t)Hkv * d, d};
   miattn_strides sv = sk;
   if (cache_strides != nullptr) {
     sk = cache_strides[0];
     sv = cache_strides[1];
   }
   if (!strides_ok(sk, 8) || !strides_ok(sv, 8)) return MIATTN_ERR_UNSUPPORTED;
-  // one (sequence, KV head) of the cache is addressed with 32-bit byte offsets
-  if ((int64_t)max_len * sk.s * 2 >= ((int64_t)1 << 31) ||
-      (int64_t)max_len * sv.s * 2 >= ((int64_t)1 << 31))
+  // one (sequence, KV head) of a contiguous cache is addressed with 32-bit
+  // byte offsets (a paged cache with 64-bit ones)
+  if (!paged && ((int64_t)max_len * sk.s * 2 >= ((int64_t)1 << 31) ||
+                 (int64_t)max_len * sv.s * 2 >= ((int64_t)1 << 31)))
     return MIATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return MIATTN_ERR_UNSUPPORTED;
 
@@ -268,6 +273,10 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   p.k_sb = sk.b; p.k_ss = sk.s; p.k_sh = sk.h;
   p.v_sb = sv.b; p.v_ss = sv.s; p.v_sh = sv.h;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.max_len = max_len; p.nt = nt;
+  p.table = table;
+  p.page_shift = 0;
+  while (paged && (1 << p.page_shift) < page_size) ++p.page_shift;
+  p.max_pages = max_pages;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.n_splits = decode_splits(Hkv, kv_splits);
   p.part_o = (float*)workspace;
@@ -279,6 +288,20 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
 }  // namespace
 
 extern "C" {
+
+int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                      const int32_t* block_table, const int32_t* seqlens, void* o, float* lse,
+                      int dtype, int B, int n_new, int Hq, int Hkv, int page_size, int max_pages,
+                      int d, float scale, int kv_splits, const miattn_strides* page_strides,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (page_size < 16 || (page_size & (page_size - 1)) != 0 || max_pages < 0)
+    return MIATTN_ERR_SHAPE;
+  if (B > 0 && block_table == nullptr) return MIATTN_ERR_NULL;
+  if ((int64_t)page_size * max_pages > INT32_MAX) return MIATTN_ERR_SHAPE;
+  return decode_impl(q, k_pages, v_pages, seqlens, o, lse, dtype, B, n_new, Hq, Hkv,
+                     page_size * max_pages, d, scale, kv_splits, page_strides, workspace,
+                     workspace_bytes, stream, block_table, page_size, max_pages);
+}
 
 int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* seqlens, void* o, float* lse, int dtype, int B, int Hq, int Hkv,

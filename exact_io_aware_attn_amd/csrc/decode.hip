@@ -31,6 +31,9 @@
 //    (the causal rule aligned at the end), so several tokens verified or
 //    generated at once share one read of the cache;
 //  * rows at or past seqlens[b] are never read;
+//  * a paged cache changes only the address of a row: each lane looks up its
+//    row's page in the sequence's block table (a small, hot array) and reads
+//    the row there; ranges, slices and the merge are the same;
 //  * partial (range i, sequence b) is stored in slot i + b: the (i, b) pairs
 //    that meet form a monotone staircase, so i + b is unique. A second kernel
 //    merges the partials of each sequence with weights exp(LSE_c - LSE)
@@ -66,7 +69,7 @@ __device__ int64_t wave_sum_lens(const int32_t* seqlens, int n, int lane) {
 }
 
 // NW: waves per workgroup = KV heads per workgroup (a divisor of Hkv)
-template <int D, int NW>
+template <int D, int NW, bool PAGED>
 __global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) decode_split_kernel(const DecodeParams p) {
   constexpr int KST = D / 32;  // k-steps (32 d each) of S^T
   constexpr int MB = D / 16;   // 16-row blocks of O^T
@@ -115,8 +118,10 @@ __global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) decode_split_ke
     if (len > 0 && end > lo) {
       const int k_begin = (int)((lo > start ? lo : start) - start);
       const int k_end = (int)((hi < end ? hi : end) - start);
-      const __bf16* kg = kbase + b * p.k_sb + lch * 8;
-      const __bf16* vg = vbase + b * p.v_sb + lch * 8;
+      const __bf16* kg = kbase + (PAGED ? 0 : b * p.k_sb) + lch * 8;
+      const __bf16* vg = vbase + (PAGED ? 0 : b * p.v_sb) + lch * 8;
+      const int32_t* tab = PAGED ? p.table + (int64_t)b * p.max_pages : nullptr;
+      const int pmask = (1 << p.page_shift) - 1;
 
       // Q^T as B operand: lane (n, g4), k-step t holds q[row n][32t + 8g4 .. +8]
       const int tok = n / G, hg = n - tok * G;
@@ -146,8 +151,15 @@ __global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) decode_split_ke
           const int key = s0 + RPL * i;
           const bool ok = key < k_end;
           u32x4 z = {0u, 0u, 0u, 0u};
-          kreg[set][i] = ok ? __builtin_nontemporal_load((const u32x4*)(kg + (int64_t)key * p.k_ss)) : z;
-          vreg[set][i] = ok ? __builtin_nontemporal_load((const u32x4*)(vg + (int64_t)key * p.v_ss)) : z;
+          int64_t ko = (int64_t)key * p.k_ss, vo = (int64_t)key * p.v_ss;
+          if constexpr (PAGED) {
+            const int64_t page = ok ? tab[key >> p.page_shift] : 0;
+            const int64_t r = key & pmask;
+            ko = page * p.k_sb + r * p.k_ss;
+            vo = page * p.v_sb + r * p.v_ss;
+          }
+          kreg[set][i] = ok ? __builtin_nontemporal_load((const u32x4*)(kg + ko)) : z;
+          vreg[set][i] = ok ? __builtin_nontemporal_load((const u32x4*)(vg + vo)) : z;
         }
       };
 
@@ -300,9 +312,12 @@ hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t s) {
   if (p.B == 0) return hipSuccess;
   const int nw = decode_waves_per_group(p.Hkv);
   const dim3 grid(p.n_splits, p.Hkv / nw);
-#define MIATTN_DECODE(DD, NWV)                                                       \
-  case NWV:                                                                          \
-    hipLaunchKernelGGL((decode_split_kernel<DD, NWV>), grid, dim3(NWV * 64), 0, s, p); \
+#define MIATTN_DECODE(DD, NWV)                                                              \
+  case NWV:                                                                                 \
+    if (p.table != nullptr)                                                                 \
+      hipLaunchKernelGGL((decode_split_kernel<DD, NWV, true>), grid, dim3(NWV * 64), 0, s, p); \
+    else                                                                                    \
+      hipLaunchKernelGGL((decode_split_kernel<DD, NWV, false>), grid, dim3(NWV * 64), 0, s, p); \
     break;
   if (d == 64) {
     switch (nw) { MIATTN_DECODE(64, 8) MIATTN_DECODE(64, 4) MIATTN_DECODE(64, 2) MIATTN_DECODE(64, 1) }

@@ -69,6 +69,10 @@ struct DecodeParams {
   int64_t v_sb, v_ss, v_sh;
   int B, Hq, Hkv, max_len;
   int nt;            // new tokens per sequence (rows of q per sequence), nt * Hq/Hkv <= 16
+  // paged cache (table != nullptr): row r of sequence b is row r % page_size of
+  // page table[b * max_pages + r / page_size]; k_sb / v_sb are then page strides
+  const int32_t* table;
+  int page_shift, max_pages;
   float scale_log2;
   int n_splits;      // ranges the flattened cache is cut into (<= kMaxSplits)
   float* part_o;     // [n_splits + B][nt][Hq][d], slot = range + batch

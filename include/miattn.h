@@ -183,6 +183,28 @@ int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
                       const miattn_strides* cache_strides, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* Decode (one or several new tokens per sequence, as attn_decode_multi)
+ * against a paged KV cache. The pages name paged caches without fixing a
+ * layout ("Attention Mechanism Optimization for Efficient LLM Inference",
+ * closing section); this one is:
+ *
+ * k_pages, v_pages  device, [num_pages, page_size, Hkv, d] bf16 (read); with
+ *          page_strides (an array of 2, k then v) "b" is the stride from page
+ *          to page, "s" from row to row, "h" from head to head, in elements
+ * block_table  device, int32 [B, max_pages]: cached row r of sequence b is
+ *          row r % page_size of page block_table[b * max_pages + r / page_size]
+ *          (precondition, not checked: entries < num_pages for every row
+ *          below seqlens[b])
+ * seqlens  device, int32 [B], each in [0, page_size * max_pages]
+ * page_size  a power of two >= 16
+ * q, o, lse, n_new, workspace  as in attn_decode_multi (workspace size from
+ *          attn_decode_multi_workspace_bytes) */
+int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                      const int32_t* block_table, const int32_t* seqlens, void* o, float* lse,
+                      int dtype, int B, int n_new, int Hq, int Hkv, int page_size, int max_pages,
+                      int d, float scale, int kv_splits, const miattn_strides* page_strides,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace attn_bwd needs: two fp32 rows of Nq rounded up
  * to 64 per (batch, query head) -- the forward LSE in base-2 units and
  * D_i = dO_i . O_i. Returns 0 for invalid sizes. */

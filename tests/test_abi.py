@@ -180,3 +180,23 @@ def test_decode_multi_workspace_scales_with_tokens():
     assert bd.attn_decode_multi_workspace_bytes(64, 1, 32, 8, 32768, 128, 0) == one
     assert bd.attn_decode_multi_workspace_bytes(64, 4, 32, 8, 32768, 128, 0) >= 4 * one - 4096
     assert bd.attn_decode_multi_workspace_bytes(64, 0, 32, 8, 32768, 128, 0) == 0
+
+
+def _decp(**kw):
+    a = dict(q=16, k=16, v=16, table=16, seqlens=16, o=16, lse=None, dtype=0, B=2, nt=1, Hq=8,
+             Hkv=2, page_size=64, max_pages=10, d=128, scale=0.1, chunk=0, ws=None, ws_bytes=0)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return bd.library().attn_decode_paged(P(a["q"]), P(a["k"]), P(a["v"]), P(a["table"]),
+                                          P(a["seqlens"]), P(a["o"]), P(a["lse"]), a["dtype"],
+                                          a["B"], a["nt"], a["Hq"], a["Hkv"], a["page_size"],
+                                          a["max_pages"], a["d"], a["scale"], a["chunk"], None,
+                                          P(a["ws"]), a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page_size=8), 2), (dict(page_size=48), 2), (dict(max_pages=-1), 2),
+    (dict(table=None), 1), (dict(nt=5), 3), (dict(d=96), 3), (dict(ws=None), 4), (dict(B=0), 0),
+])
+def test_decode_paged_validation(kw, status):
+    assert _decp(**kw) == status

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from exact_io_aware_attn_amd import attn_decode, attn_decode_multi
+from exact_io_aware_attn_amd import attn_decode, attn_decode_multi, attn_decode_paged
 from exact_io_aware_attn_amd.inputs import WORKLOADS, decode_inputs, decode_multi_inputs
 
 from parity import check, to64
@@ -165,3 +165,37 @@ def test_full_gqa_decode_b64_4tok_sampled():
         O, L = _multi_ref(ins["q"][b:b + 1].cpu(), ins["k_cache"][b:b + 1].cpu(),
                           ins["v_cache"][b:b + 1].cpu(), sl[b:b + 1].numpy(), w.scale)
         check(o[b:b + 1], O, lse[b:b + 1], L, where=f"gqa-decode-b64-4tok b={b}")
+
+
+# ------------------------------------------------------------------ paged cache
+def _to_pages(kc, vc, page_size, seed, spare=3):
+    """Scatter a contiguous cache [B, max_len, Hkv, d] into randomly placed pages
+    (plus a few unused ones) and return (k_pages, v_pages, block_table)."""
+    B, max_len, Hkv, d = kc.shape
+    mp = max_len // page_size
+    n_pages = B * mp + spare
+    perm = torch.from_numpy(np.random.default_rng(seed).permutation(n_pages)[:B * mp].astype(np.int32))
+    table = perm.view(B, mp)
+    kp = torch.zeros(n_pages, page_size, Hkv, d, dtype=kc.dtype)
+    vp = torch.zeros_like(kp)
+    kp[table.reshape(-1).long()] = kc.reshape(B * mp, page_size, Hkv, d)
+    vp[table.reshape(-1).long()] = vc.reshape(B * mp, page_size, Hkv, d)
+    return kp, vp, table
+
+
+@pytest.mark.parametrize("page_size", [16, 64, 256])
+@pytest.mark.parametrize("nt", [1, 4])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_paged(page_size, nt, d):
+    max_len = 1024
+    seqlens, q, kc, vc = decode_multi_inputs(5, nt, 8, 2, max_len, d, seed=page_size + nt + d,
+                                             len_lo=0)
+    seqlens[1] = max_len
+    kp, vp, table = _to_pages(kc, vc, page_size, seed=page_size * 7 + d)
+    o, lse = attn_decode_paged(q.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), seqlens.to(DEV))
+    o2, lse2 = attn_decode_multi(q.to(DEV), kc.to(DEV), vc.to(DEV), seqlens.to(DEV))
+    torch.cuda.synchronize()
+    # the same rows in the same order: identical to the contiguous cache, bit for bit
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    O, L = _multi_ref(q, kc, vc, seqlens.numpy(), 1 / math.sqrt(d))
+    check(o, O, lse, L, where=f"paged P={page_size} nt={nt} d={d}")
