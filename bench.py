@@ -26,7 +26,8 @@ video-frames-16x880-centered, tiny-f32, and the backward pass (attn_bwd, with
 O and the LSE from one attn_fwd call made before the timed steps; 10 d FLOPs
 per attended pair): llama3-8b-gqa-causal-8k-bwd, gpt2-medium-causal-bwd,
 video-frames-16x880-bwd; and gqa-decode-b64-4tok (attn_decode_multi, 4 new
-tokens per sequence against the cache, KV-read GB/s).
+tokens per sequence against the cache, KV-read GB/s), gqa-decode-b64-paged
+(attn_decode_paged, the decode cache in 64-row pages placed at random).
 """
 
 import argparse
@@ -134,7 +135,12 @@ class Part:
             self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
             self.seqlens_host = sl.cpu().numpy()
             self.flops, self.bytes = acc.workload_work(w, seqlens=self.seqlens_host)
-            if w.n_new > 1:
+            if w.page_size:
+                self.lse = torch.empty((w.B, 1, w.Hq), dtype=torch.float32, device=dev)
+                self.call, _, _ = bd.prepare_decode_paged(ins["q"], ins["k_pages"], ins["v_pages"],
+                                                          ins["block_table"], sl, lse_out=self.lse,
+                                                          workspace=self.ws)
+            elif w.n_new > 1:
                 self.lse = torch.empty((w.B, w.n_new, w.Hq), dtype=torch.float32, device=dev)
                 need = bd.attn_decode_multi_workspace_bytes(w.B, w.n_new, w.Hq, w.Hkv, w.Nk, w.d, 0)
                 self.ws = torch.empty(need, dtype=torch.uint8, device=dev)

@@ -143,6 +143,20 @@ __global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) decode_split_ke
       const int n_iter = (k_end - k_begin + SL - 1) / SL;
       // load instruction i of a slice: rows RPL*i + lrow, chunk lch
       u32x4 kreg[2][NL], vreg[2][NL];
+      // paged: page of each row the lane loads for the next slice, read one
+      // slice ahead of the rows themselves (so a row load never waits for its
+      // table entry, and with it for the loads issued before)
+      int tpg[NL];
+      auto load_pages = [&](int it) {
+        if constexpr (PAGED) {
+          const int s0 = k_begin + it * SL + lrow;
+#pragma unroll
+          for (int i = 0; i < NL; ++i) {
+            const int key = s0 + RPL * i;
+            tpg[i] = key < k_end ? tab[key >> p.page_shift] : 0;
+          }
+        }
+      };
       auto load_set = [&](int it, auto setc) {
         constexpr int set = decltype(setc)::value;
         const int s0 = k_begin + it * SL + lrow;
@@ -153,7 +167,7 @@ __global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) decode_split_ke
           u32x4 z = {0u, 0u, 0u, 0u};
           int64_t ko = (int64_t)key * p.k_ss, vo = (int64_t)key * p.v_ss;
           if constexpr (PAGED) {
-            const int64_t page = ok ? tab[key >> p.page_shift] : 0;
+            const int64_t page = tpg[i];
             const int64_t r = key & pmask;
             ko = page * p.k_sb + r * p.k_ss;
             vo = page * p.v_sb + r * p.v_ss;
@@ -179,7 +193,10 @@ __global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) decode_split_ke
           *(u32x4*)(sk + r * D + ksw(r, lch) * 8) = kreg[SET][i];
           *(u32x4*)(sv + r * D + vsw(r, lch) * 8) = vreg[SET][i];
         }
-        if (it + 1 < n_iter) load_set(it + 1, std::integral_constant<int, 1 - SET>());
+        if (it + 1 < n_iter) {
+          load_set(it + 1, std::integral_constant<int, 1 - SET>());
+          if (PAGED && it + 2 < n_iter) load_pages(it + 2);
+        }
         wave_lds_sync();
 
         const int s0 = k_begin + it * SL;
@@ -240,7 +257,11 @@ __global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) decode_split_ke
         wave_lds_sync();
       };
 
-      if (n_iter > 0) load_set(0, std::integral_constant<int, 0>());
+      if (n_iter > 0) {
+        load_pages(0);
+        load_set(0, std::integral_constant<int, 0>());
+        if (PAGED && n_iter > 1) load_pages(1);
+      }
       for (int it = 0; it < n_iter; it += 2) {
         step(it, std::integral_constant<int, 0>());
         if (it + 1 < n_iter) step(it + 1, std::integral_constant<int, 1>());

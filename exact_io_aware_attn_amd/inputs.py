@@ -36,6 +36,7 @@ class Workload:
     len_hi: int = 0
     softmax: tuple = field(default=("online",))
     n_new: int = 1            # decode: new tokens per sequence (causal among themselves)
+    page_size: int = 0        # decode: > 0 for a paged cache (pages placed at random)
 
     @property
     def scale(self):
@@ -71,6 +72,10 @@ WORKLOADS = {
     "gqa-decode-b64-4tok": Workload("gqa-decode-b64-4tok", "decode", B=64, Hq=32, Hkv=8, Nq=4,
                                     Nk=32768, d=128, dtype="bf16", seed=10, len_lo=1024,
                                     len_hi=32768, n_new=4),
+    # the decode workload's cache held in pages of 64 rows placed in random order
+    "gqa-decode-b64-paged": Workload("gqa-decode-b64-paged", "decode", B=64, Hq=32, Hkv=8,
+                                     Nq=1, Nk=32768, d=128, dtype="bf16", seed=4,
+                                     len_lo=1024, len_hi=32768, page_size=64),
     "gpt2-medium-causal-bwd": Workload("gpt2-medium-causal-bwd", "backward", B=64, Hq=16,
                                        Hkv=16, Nq=1024, Nk=1024, d=64, dtype="bf16",
                                        causal=True, seed=8),
@@ -135,6 +140,22 @@ def decode_inputs(B, Hq, Hkv, max_len, d, dtype=torch.bfloat16, seed=0, len_lo=1
     return seqlens, q, kc, vc
 
 
+def paged_cache(k_cache, v_cache, page_size, seed=0):
+    """The same cache rows scattered over pages [num_pages, page_size, Hkv, d] in a
+    seeded random order, with the block table int32 [B, max_len / page_size]."""
+    B, max_len, Hkv, d = k_cache.shape
+    mp = max_len // page_size
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    table = torch.randperm(B * mp, generator=g).to(torch.int32).view(B, mp).to(k_cache.device)
+    idx = table.reshape(-1).long()
+    kp = torch.empty(B * mp, page_size, Hkv, d, dtype=k_cache.dtype, device=k_cache.device)
+    vp = torch.empty_like(kp)
+    kp[idx] = k_cache.reshape(B * mp, page_size, Hkv, d)
+    vp[idx] = v_cache.reshape(B * mp, page_size, Hkv, d)
+    return kp, vp, table
+
+
 def decode_multi_inputs(B, n_new, Hq, Hkv, max_len, d, dtype=torch.bfloat16, seed=0, len_lo=1,
                         len_hi=None, device="cpu"):
     """As decode_inputs, with q [B, n_new, Hq, d] (the new tokens, whose own keys
@@ -190,4 +211,8 @@ def workload_inputs(w: Workload, device="cpu"):
     else:
         seqlens, q, kc, vc = decode_inputs(w.B, w.Hq, w.Hkv, w.Nk, w.d, w.torch_dtype,
                                            w.seed, w.len_lo, w.len_hi, device)
+    if w.page_size:
+        kp, vp, table = paged_cache(kc, vc, w.page_size, w.seed)
+        del kc, vc
+        return dict(seqlens=seqlens, q=q, k_pages=kp, v_pages=vp, block_table=table)
     return dict(seqlens=seqlens, q=q, k_cache=kc, v_cache=vc)

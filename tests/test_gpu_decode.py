@@ -199,3 +199,19 @@ def test_decode_paged(page_size, nt, d):
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
     O, L = _multi_ref(q, kc, vc, seqlens.numpy(), 1 / math.sqrt(d))
     check(o, O, lse, L, where=f"paged P={page_size} nt={nt} d={d}")
+
+
+def test_full_gqa_decode_b64_paged_equals_contiguous():
+    # same seed, same rows: the paged workload must reproduce the contiguous one bit for bit
+    from exact_io_aware_attn_amd.inputs import workload_inputs
+    w = WORKLOADS["gqa-decode-b64"]
+    ins = workload_inputs(w, device=DEV)
+    o1, l1 = attn_decode(ins["q"], ins["k_cache"], ins["v_cache"], ins["seqlens"])
+    torch.cuda.synchronize()
+    del ins
+    wp = WORKLOADS["gqa-decode-b64-paged"]
+    ins = workload_inputs(wp, device=DEV)
+    o2, l2 = attn_decode_paged(ins["q"], ins["k_pages"], ins["v_pages"], ins["block_table"],
+                               ins["seqlens"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2[:, 0]) and torch.equal(l1, l2[:, 0])

@@ -53,7 +53,7 @@ def test_named_workloads():
                               "gqa-decode-b64", "video-frames-16x880",
                               "gpt2-medium-causal", "llama3-8b-gqa-causal-8k-bwd",
                               "gpt2-medium-causal-bwd", "video-frames-16x880-bwd",
-                              "gqa-decode-b64-4tok"}
+                              "gqa-decode-b64-4tok", "gqa-decode-b64-paged"}
     assert WORKLOADS["llama3-8b-gqa-causal-8k"].scale == 1 / 128 ** 0.5
 
 
@@ -64,3 +64,12 @@ def test_backward_inputs_extend_the_prefill_draws():
     q2, k2, v2, do = backward_inputs(2, 4, 2, 33, 40, 64, torch.bfloat16, seed=9)
     assert torch.equal(q, q2) and torch.equal(k, k2) and torch.equal(v, v2)
     assert do.shape == q.shape and not torch.equal(do, q)
+
+
+def test_paged_cache_holds_the_same_rows():
+    from exact_io_aware_attn_amd.inputs import decode_inputs, paged_cache
+    _, _, kc, vc = decode_inputs(3, 4, 2, 128, 64, torch.bfloat16, seed=5)
+    kp, vp, table = paged_cache(kc, vc, 32, seed=2)
+    assert table.shape == (3, 4) and sorted(table.reshape(-1).tolist()) == list(range(12))
+    assert torch.equal(kp[table.long()].reshape(kc.shape), kc)
+    assert torch.equal(vp[table.long()].reshape(vc.shape), vc)
