@@ -204,6 +204,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     p.ks.part_max = part_max;
     p.ks.kbar = kbar;
     p.ks.nsplit = nsplit;
+    p.ks.keys_per_split = kp.keys_per_split;
   }
 
   hipError_t e = dtype == MIATTN_BF16 ? miattn::launch_fwd_bf16(p, d, causal, block, s)

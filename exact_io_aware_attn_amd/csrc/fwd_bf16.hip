@@ -257,7 +257,12 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
     const float qn = sqrtf(qq);
     // rho^2 = max over the key splits of the partial maxima
     const int64_t bh = (int64_t)b * p.Hkv + hkv;
-    float r2 = lane < p.ks.nsplit ? p.ks.part_max[bh * kMaxSplit + lane] : 0.f;
+    // causal: only the key splits the wave's rows can see (those starting at
+    // or before its last visible key) enter the bound, a tighter bound for
+    // the early rows; block masks take every split
+    bool seen = lane < p.ks.nsplit;
+    if (CAUSAL && !BLOCK) seen = seen && lane * p.ks.keys_per_split <= wave_last + p.causal_off;
+    float r2 = seen ? p.ks.part_max[bh * kMaxSplit + lane] : 0.f;
     r2 = wave_max(r2);
     const float rho = sqrtf(r2);
     float qk = 0.f;

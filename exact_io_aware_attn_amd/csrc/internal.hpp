@@ -24,6 +24,7 @@ struct KStats {
   const float* part_max;  // [B*Hkv][kMaxSplit], max |k|^2 or |k - kbar|^2
   const float* kbar;      // [B*Hkv][d] mean key (centred mode) or nullptr
   int nsplit;
+  int keys_per_split;     // split s covers keys [s * keys_per_split, (s + 1) * keys_per_split)
 };
 
 struct FwdParams {

@@ -395,3 +395,19 @@ def test_full_llama3_8b_gqa_causal():
 @pytest.mark.parametrize("mode", ["online", "fixed_max"])
 def test_full_video_frames(mode):
     _full("video-frames-16x880", mode=mode, heads=[0, 13, 23])
+
+
+@pytest.mark.parametrize("mode", ["fixed_max", "fixed_max_centered"])
+def test_bf16_fixed_max_causal_large_late_keys(mode):
+    # the last 64 keys are 3x longer: with a bound over every key the early
+    # 32-row groups' gap (about 2 scale |q| max|k| = 84 nats) exceeds the 64-nat
+    # limit; under the causal rule only the last rows see those keys, so the
+    # bound over the splits a wave can see keeps the early groups eligible.
+    # Their values are shrunk so the peaked last rows keep outputs of moderate
+    # size (the bf16 rounding of a large output would dominate the error).
+    q, k, v = prefill_inputs(2, 4, 2, 700, 700, 128, torch.bfloat16, seed=77)
+    k[:, -64:] = (k[:, -64:].float() * 3).to(torch.bfloat16)
+    v[:, -64:] = (v[:, -64:].float() * 0.25).to(torch.bfloat16)
+    o, lse = _run(q, k, v, causal=True, softmax=mode)
+    O, L = _ref(q, k, v, 1 / math.sqrt(128), causal=True)
+    check(o, O, lse, L, where=f"{mode} causal large late keys")
