@@ -80,24 +80,29 @@ def library():
 
 
 def attn_status_str(status):
+    """Static description of a status code returned by the library."""
     return library().attn_status_str(int(status)).decode()
 
 
 def attn_fwd_workspace_bytes(B, Hkv, Nq, Nk, d, mask_kind, block_q, softmax_mode):
+    """Workspace bytes attn_fwd needs for these arguments (0 for the plain online mode)."""
     return int(library().attn_fwd_workspace_bytes(B, Hkv, Nq, Nk, d, mask_kind, block_q,
                                                   softmax_mode))
 
 
 def attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d, kv_splits=0):
+    """Workspace bytes attn_decode needs (the split-K partial results)."""
     return int(library().attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d, kv_splits))
 
 
 def attn_decode_multi_workspace_bytes(B, n_new, Hq, Hkv, max_len, d, kv_splits=0):
+    """Workspace bytes attn_decode_multi and attn_decode_paged need."""
     return int(library().attn_decode_multi_workspace_bytes(B, n_new, Hq, Hkv, max_len, d,
                                                            kv_splits))
 
 
 def attn_bwd_workspace_bytes(B, Hq, Nq):
+    """Workspace bytes attn_bwd needs (per-row statistics of the backward pass)."""
     return int(library().attn_bwd_workspace_bytes(B, Hq, Nq))
 
 
