@@ -72,9 +72,6 @@ __device__ __forceinline__ int block_state(const BwdParams& p, int q_lo, int q_h
     }
   return !any ? 0 : all ? 1 : 2;
 }
-__device__ __forceinline__ bool pair_live(const BwdParams& p, int q, int key) {
-  return p.block_mask[(int64_t)(q / p.block_q) * p.nkb + key / p.block_k] != 0;
-}
 
 // Block mask: the streamed tiles (64 rows of queries or keys) that meet a live
 // block of the workgroup's stationary range, compacted in order into list[]
@@ -269,8 +266,25 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
     }
   };
   // P = exp2(c s - lse2) into s and dS = P (dP - D) into dp, rows 8j + 4h + i
+  const int key_blk = (BLOCK && key_ok) ? key / p.block_k : 0;  // this lane's mask column
   auto softmax = [&](const float* ss, int qb, int qs, bool masked, f32x16& s, f32x16& dp)
       __attribute__((always_inline)) {
+    // block mask, mixed region: the 32 rows span at most three block rows;
+    // their flags for this lane's key block are read once, and each row picks
+    // one by comparing with the block-row boundaries
+    bool fl0 = false, fl1 = false, fl2 = false;
+    int qbb1 = 0, qbb2 = 0;
+    if (BLOCK && masked) {
+      const int qb0 = qs / p.block_q, nqb = p.Nq / p.block_q;
+      qbb1 = (qb0 + 1) * p.block_q;
+      qbb2 = (qb0 + 2) * p.block_q;
+      const uint8_t* col = p.block_mask + key_blk;
+      if (key_ok) {
+        fl0 = col[(int64_t)qb0 * p.nkb] != 0;
+        fl1 = qb0 + 1 < nqb && col[(int64_t)(qb0 + 1) * p.nkb] != 0;
+        fl2 = qb0 + 2 < nqb && col[(int64_t)(qb0 + 2) * p.nkb] != 0;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const f32x4 l4 = *(const f32x4*)(ss + 32 * qb + 8 * j + 4 * h);
@@ -283,7 +297,7 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
           const int q = qs + 8 * j + 4 * h + i;
           bool ok = true;
           if (CAUSAL) ok = key <= q + p.causal_off;
-          if (BLOCK) ok = ok && q < p.Nq && key_ok && pair_live(p, q, key);
+          if (BLOCK) ok = ok && q < p.Nq && (q >= qbb2 ? fl2 : q >= qbb1 ? fl1 : fl0);
           pr = ok ? pr : 0.f;
         }
         s[r] = pr;
@@ -523,6 +537,7 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
   const int qrow = q0 + qc;
   const bool row_ok = qrow < p.Nq;
   const int wave_last = min(q0 + 31, p.Nq - 1);
+  const int row_blk = (BLOCK && row_ok) ? qrow / p.block_q : 0;  // this lane's mask row
 
   bf16x8 qf[KSTEPS], gf[KSTEPS];
   {
@@ -714,6 +729,17 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
         dp[kb] = mfma32(row_frag<D, false>(sv, kb, ks, qc, h), gf[ks], dp[kb]);
       }
     }
+    // block mask, mixed region: the tile's 64 keys span at most five key
+    // blocks; their flags for this lane's row block are read once, and each
+    // key picks one by comparing with the key-block boundaries
+    bool fl[5] = {false, false, false, false, false};
+    int kb0 = 0;
+    if (BLOCK && state == 2) {
+      kb0 = k0 / p.block_k;
+      const uint8_t* rowm = p.block_mask + (int64_t)row_blk * p.nkb;
+#pragma unroll
+      for (int x = 0; x < 5; ++x) fl[x] = row_ok && kb0 + x < p.nkb && rowm[kb0 + x] != 0;
+    }
     // dS^T = P^T (dP^T - D) in place of dP^T
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -724,7 +750,11 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
           const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
           bool ok = kk < p.Nk;
           if (CAUSAL) ok = ok && kk <= qrow + p.causal_off;
-          if (BLOCK) ok = ok && row_ok && pair_live(p, qrow, kk);
+          if (BLOCK) {
+            const int x = (kk >= (kb0 + 1) * p.block_k) + (kk >= (kb0 + 2) * p.block_k) +
+                          (kk >= (kb0 + 3) * p.block_k) + (kk >= (kb0 + 4) * p.block_k);
+            ok = ok && (x == 0 ? fl[0] : x == 1 ? fl[1] : x == 2 ? fl[2] : x == 3 ? fl[3] : fl[4]);
+          }
           pr = ok ? pr : 0.f;
         }
         dp[kb][r] = pr * (dp[kb][r] - dsum);
