@@ -12,7 +12,9 @@ What it computes (each function cites the page passage it follows):
 * ``decode``         -- one new query per sequence against a KV cache.
 * ``logit_bound``    -- the Cauchy-Schwarz upper bound on each row's logits
                         (optionally with mean-centred keys).
-* ``fixed_max_eligible`` -- the per-row-group eligibility rule for that bound.
+* ``fixed_max_bounds`` -- the per-row bound over the keys a row can see,
+                        its gap to the row max and the eligibility rule.
+* ``round_to_bf16``   -- round to the nearest bfloat16 (ties to even).
 * ``fixed_max_attention`` -- softmax evaluated against the bound instead of the
                         row maximum (equal to ``attention`` in exact arithmetic).
 * ``online_softmax``  -- the running (max, sum) recurrence over blocks of a row.
@@ -41,8 +43,9 @@ from .attention import (  # noqa: F401
     decode,
     element_mask,
     fixed_max_attention,
-    fixed_max_eligible,
+    fixed_max_bounds,
     logit_bound,
     merge_partials,
     online_softmax,
+    round_to_bf16,
 )

@@ -25,7 +25,7 @@ chunks; rows are independent, so chunking changes nothing.
 import numpy as np
 
 # Eligibility threshold for the fixed-max softmax, in nats. Parity unpinned:
-# chosen here, not given by the pages (see fixed_max_eligible).
+# chosen here, not given by the pages (see fixed_max_bounds).
 TAU = 64.0
 
 _ROW_CHUNK = 2048
@@ -180,23 +180,106 @@ def logit_bound(q, k, scale, *, centered=False):
     return M
 
 
-def fixed_max_eligible(qnorm_rows, rho, scale, tau=TAU):
-    """Eligibility of a group of query rows for the fixed-max softmax.
+def round_to_bf16(x):
+    """Round float64 values to the nearest bfloat16 (ties to even), as float64.
 
-    TPU attention guide, 4단계: a bound far above the true row max pushes the
-    exponentials toward underflow, so each group is checked and falls back to
-    the running-max softmax when the bound is loose. Every logit of row i lies
-    in [M_i - 2 * scale * |q_i| * rho, M_i], where rho = max_j |k_j| for the
-    plain bound and max_j |k_j - kbar| for the centred one (Cauchy-Schwarz from
-    both sides). So the row's largest term exp(s_max - M_i) is at least
-    exp(-2 * scale * |q_i| * rho). Rule: eligible iff
-    2 * scale * max_i |q_i| * rho <= tau; then every row normaliser is at least
-    exp(-tau), far above the float32 minimum normal exp(-87.3).
+    The value is first rounded to float32 (nearest even), then to the 8-bit
+    significand of bfloat16 by rounding the low 16 bits of its float32 pattern
+    to nearest, ties to even. Finite inputs only."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
-    Parity unpinned: tau (default 64 nats) is chosen here.
+
+def fixed_max_bounds(q, k, scale, *, centered=False, causal=False, block_mask=None,
+                     block_q=None, block_k=None, key_block=256, tau=TAU):
+    """Per-row fixed reference M_i, its gap and eligibility, from the keys the
+    row can see (TPU attention guide, 4단계).
+
+    The guide bounds a row's logits before any key block is read: by
+    Cauchy-Schwarz q . k <= |q| |k|, and with a centre c, q . k = q . c +
+    q . (k - c) <= q . c + |q| |k - c| (centring tightens the bound and leaves
+    the softmax unchanged). It takes one bound per head over all keys; any
+    upper bound gives the same exact softmax, and this reading takes the
+    bound over the keys the row can see only, so that keys a mask excludes
+    never influence the row, and checks eligibility per row (finer than the
+    guide's per-head check, equally sound).
+
+    The keys of each (batch, KV head) are cut into blocks: the block mask's
+    block_k when there is one, else key_block keys. A block meets row i if the
+    row sees at least one of its keys; it is "full" if the row sees all of
+    them. With N_j = |k_j|, for each block b meeting the row:
+
+    * full, plain: upper = |q| max_b N_j, lower = -upper;
+    * full, centred: c_b = the mean of the block's keys rounded to bfloat16,
+      R_b = max_b |k_j - c_b|; upper = q . c_b + |q| R_b, lower = q . c_b - |q| R_b;
+    * partial (causal cuts the block): upper = |q| max N_j over the keys the
+      row sees, lower = -upper.
+
+    Each key of the row lies in some block b, so every visible logit is at most
+    M_i = scale * max_b upper; each block holds a visible key whose logit is at
+    least scale * lower, so the row's max logit is at least scale * max_b lower.
+    gap_i = M_i - scale * max_b lower bounds how far the row max sits below
+    M_i, the row's normaliser against M_i is at least exp(-gap_i), and the row
+    is eligible iff it sees a key and gap_i <= tau (then that normaliser stays
+    far above the float32 minimum normal exp(-87.3)). Parity unpinned: tau
+    (default 64 nats) is chosen here.
+
+    Returns (M, gap, eligible), each [B, Hq, Nq]; rows that see no key get
+    M = -inf, gap = nan, eligible = False.
     """
-    qn = np.asarray(qnorm_rows, dtype=np.float64)
-    return bool(2.0 * scale * qn.max() * float(rho) <= tau)
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    group = _check_heads(Hq, Hkv)
+    kb_size = int(block_k) if block_mask is not None else int(key_block)
+    nkb = (Nk + kb_size - 1) // kb_size
+    pad = nkb * kb_size - Nk
+    exists = np.concatenate([np.ones(Nk, dtype=bool), np.zeros(pad, dtype=bool)])
+    exists = exists.reshape(nkb, kb_size)
+    M = np.full((B, Hq, Nq), -np.inf)
+    gap = np.full((B, Hq, Nq), np.nan)
+    elig = np.zeros((B, Hq, Nq), dtype=bool)
+    for b in range(B):
+        for hk in range(Hkv):
+            K = k[b, :, hk, :]
+            Kp = np.concatenate([K, np.zeros((pad, d))]).reshape(nkb, kb_size, d)
+            N = np.sqrt((Kp * Kp).sum(-1))                      # [nkb, kb]
+            cnt = exists.sum(-1)                                # keys per block
+            C = round_to_bf16(Kp.sum(1) / cnt[:, None])         # [nkb, d]
+            R = np.where(exists, np.sqrt(((Kp - C[:, None, :]) ** 2).sum(-1)), -np.inf).max(-1)
+            for h in range(hk * group, (hk + 1) * group):
+                for r0 in range(0, Nq, _ROW_CHUNK):
+                    rows = np.arange(r0, min(Nq, r0 + _ROW_CHUNK))
+                    Q = q[b, rows, h, :]
+                    qn = np.sqrt((Q * Q).sum(-1))[:, None]                 # [rows, 1]
+                    allowed = element_mask(Nq, Nk, causal=causal, block_mask=block_mask,
+                                           block_q=block_q, block_k=block_k, rows=rows)
+                    A = np.concatenate([allowed, np.zeros((rows.size, pad), dtype=bool)], 1)
+                    A = A.reshape(rows.size, nkb, kb_size)
+                    meets = A.any(-1)                                      # [rows, nkb]
+                    full = meets & (A | ~exists[None]).all(-1)
+                    nvis = np.where(A, N[None], -np.inf).max(-1)           # [rows, nkb]
+                    nvis = np.where(meets, nvis, 0.0)
+                    if centered:
+                        qc = Q @ C.T
+                        up_full, lo_full = qc + qn * R[None], qc - qn * R[None]
+                    else:
+                        up_full, lo_full = qn * nvis, -qn * nvis
+                    up = np.where(full, up_full, qn * nvis)
+                    lo = np.where(full, lo_full, -qn * nvis)
+                    up = np.where(meets, up, -np.inf).max(-1)
+                    lo = np.where(meets, lo, -np.inf).max(-1)
+                    live = meets.any(-1)
+                    Mi = np.where(live, scale * up, -np.inf)
+                    with np.errstate(invalid="ignore"):
+                        gi = np.where(live, scale * (up - lo), np.nan)
+                    M[b, h, rows] = Mi
+                    gap[b, h, rows] = gi
+                    elig[b, h, rows] = live & (np.nan_to_num(gi, nan=np.inf) <= tau)
+    return M, gap, elig
 
 
 def fixed_max_attention(q, k, v, scale, M, *, causal=False, block_mask=None,

@@ -335,32 +335,162 @@ def test_fixed_max_softmax_equals_running_max(centered):
     np.testing.assert_allclose(L2, L, atol=1e-12)
 
 
+def _scores(q, k, scale):
+    """[B, Hq, Nq, Nk] scaled scores, GQA heads expanded (einsum, not the oracle)."""
+    g = q.shape[2] // k.shape[2]
+    return scale * np.einsum("bihd,bjhd->bhij", q, np.repeat(k, g, axis=2))
+
+
+_MASKS = {
+    "none": {},
+    "causal": dict(causal=True),
+    "block": dict(block_mask=np.array([[1, 0, 1, 1], [0, 1, 0, 1], [1, 1, 0, 0]], np.uint8),
+                  block_q=16, block_k=16),
+    "causal+block": dict(causal=True,
+                         block_mask=np.array([[1, 1, 0, 1], [1, 0, 1, 1], [0, 1, 1, 1]], np.uint8),
+                         block_q=16, block_k=16),
+}
+
+
+@pytest.mark.parametrize("centered", [False, True])
+@pytest.mark.parametrize("mask", list(_MASKS))
+def test_fixed_max_bounds_bracket_the_row_max(centered, mask):
+    """Cauchy-Schwarz from both sides (TPU guide, 4단계): every visible logit of
+    row i is at most M_i, and the row's largest visible logit is at least
+    M_i - gap_i, so its normaliser against M_i is at least exp(-gap_i). Keys
+    with a common offset, blocks of 24 keys (several blocks, partial ones under
+    the causal rule), Nq != Nk."""
+    kw = _MASKS[mask]
+    q = _randn(2, 48, 4, 16)
+    k = _randn(2, 64, 2, 16) + 0.7
+    M, gap, el = oracle.fixed_max_bounds(q, k, 0.3, centered=centered, key_block=24, **kw)
+    S = _scores(q, k, 0.3)
+    allowed = oracle.element_mask(48, 64, **kw)[None, None]
+    live = np.broadcast_to(allowed.any(-1), M.shape)
+    assert (live == np.isfinite(M)).all()
+    Sa = np.where(allowed, S, -np.inf)
+    assert (Sa <= M[..., None] + 1e-12).all()
+    rmax = Sa.max(-1)
+    assert (rmax[live] >= (M - gap)[live] - 1e-12).all()
+    l = np.where(allowed, np.exp(S - np.where(live, M, 0)[..., None]), 0).sum(-1)
+    assert (l[live] >= np.exp(-gap[live]) * (1 - 1e-12)).all()
+    assert not el[~live].any()
+
+
+@pytest.mark.parametrize("centered", [False, True])
+def test_fixed_max_bounds_ignore_keys_the_row_cannot_see(centered):
+    """The bound of a row depends on its visible keys only: keys past the causal
+    limit of rows 0..t, and the keys of a block row's dead blocks, can change
+    (to 5x longer ones, with an offset) without changing M, gap or eligibility
+    of those rows -- the premise of excluding masked keys bit-exactly."""
+    q = _randn(1, 64, 2, 16)
+    k = _randn(1, 64, 1, 16)
+    t = 29
+    k2 = k.copy()
+    k2[:, t + 1:] = 5 * k2[:, t + 1:] + 2
+    for kw in (dict(causal=True), dict(causal=True, key_block=16), dict(causal=True, key_block=7)):
+        a = oracle.fixed_max_bounds(q, k, 0.25, centered=centered, **kw)
+        b = oracle.fixed_max_bounds(q, k2, 0.25, centered=centered, **kw)
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(x[..., :t + 1], y[..., :t + 1])
+        assert not np.array_equal(a[0][..., t + 1:], b[0][..., t + 1:])
+    bm = np.array([[1, 0, 1, 0], [0, 1, 1, 0], [1, 1, 1, 1], [0, 0, 1, 0]], np.uint8)
+    kb = dict(block_mask=bm, block_q=16, block_k=16)
+    k3 = k.copy()
+    k3[:, 16:32] = 5 * k3[:, 16:32] + 2   # key block 1: dead for block rows 0 and 3
+    a = oracle.fixed_max_bounds(q, k, 0.25, centered=centered, **kb)
+    b = oracle.fixed_max_bounds(q, k3, 0.25, centered=centered, **kb)
+    for x, y in zip(a, b):
+        for rows in (slice(0, 16), slice(48, 64)):
+            np.testing.assert_array_equal(x[..., rows], y[..., rows])
+    assert not np.array_equal(a[0][..., 16:32], b[0][..., 16:32])
+
+
+def test_fixed_max_bounds_reduce_to_the_page_bound():
+    """With no mask and all keys in one block the plain bound is the guide's
+    scale * |q_i| * max_j |k_j| (logit_bound) with gap 2 M_i; the centred one is
+    within |q_i| |c - kbar| of logit_bound's centred form (c is kbar rounded
+    to bfloat16)."""
+    q = _randn(2, 30, 4, 32)
+    k = _randn(2, 50, 2, 32) + 1.0
+    M, gap, _ = oracle.fixed_max_bounds(q, k, 0.2, key_block=64)
+    np.testing.assert_allclose(M, oracle.logit_bound(q, k, 0.2), rtol=1e-13)
+    np.testing.assert_allclose(gap, 2 * M, rtol=1e-13)
+    Mc, _, _ = oracle.fixed_max_bounds(q, k, 0.2, centered=True, key_block=64)
+    Mp = oracle.logit_bound(q, k, 0.2, centered=True)
+    kbar = k.mean(axis=1)                                          # [B, Hkv, d]
+    slack = np.linalg.norm(kbar - oracle.round_to_bf16(kbar), axis=-1)  # [B, Hkv]
+    qn = np.linalg.norm(q, axis=-1).transpose(0, 2, 1)             # [B, Hq, Nq]
+    tol = 0.2 * 2 * qn * np.repeat(slack, 2, axis=1)[..., None] + 1e-12
+    assert (np.abs(Mc - Mp) <= tol).all()
+
+
+def test_fixed_max_bounds_tight_for_query_parallel_to_longest_visible_key():
+    """q_i parallel to the longest key the row sees: the plain bound equals that
+    logit, even with a 10x longer key just past the row's causal limit."""
+    k = _randn(1, 40, 1, 16)
+    q = np.zeros((1, 40, 1, 16))
+    i = 25
+    j = int(np.argmax((k[0, :i + 1, 0] ** 2).sum(-1)))
+    k[0, i + 1, 0] *= 10
+    q[0, i, 0] = 1.5 * k[0, j, 0]
+    M, _, _ = oracle.fixed_max_bounds(q, k, 0.3, causal=True, key_block=8)
+    s = 0.3 * float(q[0, i, 0] @ k[0, j, 0])
+    assert abs(M[0, 0, i] - s) <= 1e-12 * abs(s)
+
+
 def test_eligible_rows_keep_normaliser_far_from_underflow():
     """Soundness of the eligibility rule: when it says yes, every row's
     normaliser against the bound is at least exp(-tau)."""
     d, scale = 128, 1 / math.sqrt(128)
     q, k = _randn(1, 64, 1, d), _randn(1, 256, 1, d)
-    qn = np.sqrt((q[0, :, 0] ** 2).sum(-1))
-    kmax = np.sqrt((k[0, :, 0] ** 2).sum(-1)).max()
-    assert oracle.fixed_max_eligible(qn, kmax, scale)
-    M = oracle.logit_bound(q, k, scale)
-    S = scale * q[0, :, 0] @ k[0, :, 0].T
-    l = np.exp(S - M[0, 0][:, None]).sum(-1)
-    assert (l >= math.exp(-oracle.TAU)).all()
+    for centered in (False, True):
+        M, gap, el = oracle.fixed_max_bounds(q, k, scale, centered=centered, causal=True)
+        assert el.all()
+        S = np.where(np.tril(np.ones((64, 256), bool), 192), scale * q[0, :, 0] @ k[0, :, 0].T,
+                     -np.inf)
+        l = np.exp(S - M[0, 0][:, None]).sum(-1)
+        assert (l >= math.exp(-oracle.TAU)).all()
 
 
 def test_scaled_queries_are_ineligible_and_would_underflow():
     """Queries x10 at d = 128 make the bound loose by far more than the float32
-    exponent range: the rule must refuse them (the fallback case)."""
+    exponent range: the rule must refuse them (the fallback case). Scaling
+    one head only leaves the other eligible."""
     d, scale = 128, 1 / math.sqrt(128)
-    q, k = 10 * _randn(1, 64, 1, d), _randn(1, 512, 1, d)
-    qn = np.sqrt((q[0, :, 0] ** 2).sum(-1))
-    kmax = np.sqrt((k[0, :, 0] ** 2).sum(-1)).max()
-    assert not oracle.fixed_max_eligible(qn, kmax, scale)
-    M = oracle.logit_bound(q, k, scale)
-    S = scale * q[0, :, 0] @ k[0, :, 0].T
-    gap = M[0, 0] - S.max(-1)
-    assert gap.max() > 87.4  # exp(-gap) would be below the float32 minimum normal
+    q, k = _randn(1, 64, 2, d), _randn(1, 512, 1, d)
+    q[:, :, 1] *= 10
+    M, gap, el = oracle.fixed_max_bounds(q, k, scale)
+    assert el[0, 0].all() and not el[0, 1].any()
+    S = scale * q[0, :, 1] @ k[0, :, 0].T
+    assert (M[0, 1] - S.max(-1)).max() > 87.4  # exp(-gap) would be below the fp32 minimum normal
+
+
+def test_rows_without_keys_are_ineligible():
+    q, k = _randn(1, 10, 1, 8), _randn(1, 4, 1, 8)
+    M, gap, el = oracle.fixed_max_bounds(q, k, 0.5, causal=True)   # rows 0..5 see nothing
+    assert np.isneginf(M[0, 0, :6]).all() and not el[0, 0, :6].any() and el[0, 0, 6:].all()
+
+
+def test_round_to_bf16_matches_torch():
+    """Library pin: torch's float32 -> bfloat16 conversion (nearest, ties to even)."""
+    x = np.concatenate([_randn(4000) * 10.0 ** rng.integers(-6, 6, 4000),
+                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -1 - 2 ** -8, 0.0, 65504.0])])
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.round_to_bf16(x), ref)
+
+
+@pytest.mark.parametrize("centered", [False, True])
+def test_fixed_max_softmax_with_visible_key_bound_equals_running_max(centered):
+    """Shift invariance with the per-row bound (TPU guide, 4단계): the softmax
+    against M_i is the exact softmax."""
+    q, k, v = _randn(2, 40, 4, 16), _randn(2, 33, 2, 16) + 0.5, _randn(2, 33, 2, 16)
+    M, _, _ = oracle.fixed_max_bounds(q, k, 0.25, centered=centered, causal=True, key_block=8)
+    O, L = oracle.attention(q, k, v, 0.25, causal=True)
+    O2, L2 = oracle.fixed_max_attention(q, k, v, 0.25, np.where(np.isfinite(M), M, 0.0),
+                                        causal=True)
+    np.testing.assert_allclose(O2, O, atol=1e-12)
+    np.testing.assert_allclose(L2, L, atol=1e-12)
 
 
 # ---------------------------------------------------------------- brute force
