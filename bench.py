@@ -110,7 +110,7 @@ class Part:
             mode = bd.SOFTMAX_MODES[self.softmax]
             kind = (bd.MIATTN_MASK_CAUSAL if w.causal else 0) | (
                 bd.MIATTN_MASK_BLOCK if self.bm is not None else 0)
-            need = bd.attn_fwd_workspace_bytes(w.B, w.Hkv, w.Nq, w.Nk, w.d, kind, w.block, mode)
+            need = bd.attn_fwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, kind, w.block, w.block, mode)
             self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
             self.flops, self.bytes = acc.workload_work(w, block_mask=bm)
             # arguments marshalled once; each step is one call into the library

@@ -52,7 +52,7 @@ def library():
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_status_str.argtypes = [I]
     lib.attn_status_str.restype = ctypes.c_char_p
-    lib.attn_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+    lib.attn_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I, I, I]
     lib.attn_fwd_workspace_bytes.restype = Z
     lib.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, I, I, I,
                              ctypes.POINTER(_Strides), P, Z, P]
@@ -84,10 +84,10 @@ def attn_status_str(status):
     return library().attn_status_str(int(status)).decode()
 
 
-def attn_fwd_workspace_bytes(B, Hkv, Nq, Nk, d, mask_kind, block_q, softmax_mode):
+def attn_fwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, mask_kind, block_q, block_k, softmax_mode):
     """Workspace bytes attn_fwd needs for these arguments (0 for the plain online mode)."""
-    return int(library().attn_fwd_workspace_bytes(B, Hkv, Nq, Nk, d, mask_kind, block_q,
-                                                  softmax_mode))
+    return int(library().attn_fwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, mask_kind, block_q,
+                                                  block_k, softmax_mode))
 
 
 def attn_decode_workspace_bytes(B, Hq, Hkv, max_len, d, kv_splits=0):
@@ -167,7 +167,7 @@ def _fwd_setup(q, k, v, causal, block_mask, block, scale, softmax, return_lse, o
     lse = None
     if return_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev) if lse_out is None else lse_out
-    need = attn_fwd_workspace_bytes(B, Hkv, Nq, Nk, d, mask_kind, bq, mode)
+    need = attn_fwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, mask_kind, bq, bk, mode)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     st = (_Strides * 4)(_strides4(q), _strides4(k), _strides4(v), _strides4(o))
@@ -188,6 +188,14 @@ def attn_fwd(q, k, v, *, causal=False, block_mask=None, block=None, scale=None,
     if rc != 0:
         raise MiattnError(rc, "attn_fwd")
     return o, lse
+
+
+def fixed_max_decisions(workspace, B, Hq, Hkv, Nq, Nk):
+    """The per-row choices attn_fwd recorded in a fixed-max call's workspace
+    (the layout include/miattn.h documents): a uint8 [B, Hq, Nq] view, 1 where
+    the row took the fixed max, 0 where it fell back to the running max."""
+    off = (B * Hkv * Nk * 4 + 255) // 256 * 256
+    return workspace[off:off + B * Hq * Nq].view(B, Hq, Nq)
 
 
 class PreparedCall:

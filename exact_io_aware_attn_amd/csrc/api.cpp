@@ -14,28 +14,37 @@
 namespace {
 
 using miattn::kMaxLiveBlocks;
-using miattn::kMaxSplit;
 
 constexpr size_t kAlign = 256;
+// keys per block of the fixed-max key statistics without a block mask
+constexpr int kKeyBlock = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-int kstat_splits(int Nk) {
-  int n = (Nk + 255) / 256;
-  if (n < 1) n = 1;
-  if (n > kMaxSplit) n = kMaxSplit;
-  return n;
-}
+// Workspace of the fixed-max modes, in this order (each part 256-byte
+// aligned): pmax fp32 [B*Hkv][Nk], flags uint8 [B][Hq][Nq], then in centred
+// mode radius fp32 [B*Hkv][nkb] and centre bf16 [B*Hkv][nkb][d].
+struct FwdWs {
+  size_t pmax = 0, flags = 0, radius = 0, centre = 0, total = 0;
+  int kb_size = 0, nkb = 0;
+};
 
-// Workspace of the fixed-max pre-pass, in this order:
-// part_max [B*Hkv][kMaxSplit], kbar [B*Hkv][d], part_sum [B*Hkv][kMaxSplit][d].
-size_t fwd_ws(int B, int Hkv, int d, int mode) {
-  if (mode == MIATTN_SOFTMAX_ONLINE) return 0;
+FwdWs fwd_ws(int B, int Hq, int Hkv, int Nq, int Nk, int d, int mask_kind, int block_k,
+             int mode) {
+  FwdWs w;
+  if (mode == MIATTN_SOFTMAX_ONLINE || Nk <= 0) return w;
+  w.kb_size = (mask_kind & MIATTN_MASK_BLOCK) && block_k > 0 ? block_k : kKeyBlock;
+  w.nkb = (Nk + w.kb_size - 1) / w.kb_size;
   const size_t bh = (size_t)B * Hkv;
-  size_t n = align_up(bh * kMaxSplit * sizeof(float));
-  if (mode == MIATTN_SOFTMAX_FIXED_MAX_CENTERED)
-    n += align_up(bh * d * sizeof(float)) + align_up(bh * kMaxSplit * d * sizeof(float));
-  return n;
+  w.pmax = 0;
+  w.flags = align_up(bh * Nk * sizeof(float));
+  w.total = w.flags + align_up((size_t)B * Hq * Nq);
+  if (mode == MIATTN_SOFTMAX_FIXED_MAX_CENTERED) {
+    w.radius = w.total;
+    w.centre = w.radius + align_up(bh * w.nkb * sizeof(float));
+    w.total = w.centre + align_up(bh * w.nkb * d * 2);
+  }
+  return w;
 }
 
 // Segment table of a block mask whose block_q is not a multiple of 32
@@ -95,11 +104,11 @@ const char* attn_status_str(int status) {
   }
 }
 
-size_t attn_fwd_workspace_bytes(int B, int Hkv, int Nq, int Nk, int d, int mask_kind,
-                                int block_q, int softmax_mode) {
-  (void)Nk;
-  if (B < 0 || Hkv < 0 || Nq < 0 || d <= 0) return 0;
-  return fwd_ws(B, Hkv, d, softmax_mode) + seg_ws(Nq, mask_kind, block_q);
+size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int mask_kind,
+                                int block_q, int block_k, int softmax_mode) {
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || d <= 0) return 0;
+  return fwd_ws(B, Hq, Hkv, Nq, Nk, d, mask_kind, block_k, softmax_mode).total +
+         seg_ws(Nq, mask_kind, block_q);
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
@@ -153,7 +162,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if ((int64_t)Nk * sk.s * esz >= ((int64_t)1 << 31) || (int64_t)Nk * sv.s * esz >= ((int64_t)1 << 31))
     return MIATTN_ERR_UNSUPPORTED;
 
-  const size_t ks_bytes = fwd_ws(B, Hkv, d, softmax_mode);
+  const FwdWs fw = fwd_ws(B, Hq, Hkv, Nq, Nk, d, mask_kind, block_k, softmax_mode);
+  const size_t ks_bytes = fw.total;
   const size_t need = ks_bytes + seg_ws(Nq, mask_kind, block_q);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MIATTN_ERR_WORKSPACE;
 
@@ -182,29 +192,23 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   }
 
   if (p.fixed != MIATTN_SOFTMAX_ONLINE) {
-    const size_t bh = (size_t)B * Hkv;
     char* ws = (char*)workspace;
-    float* part_max = (float*)ws;
-    float* kbar = nullptr;
-    float* part_sum = nullptr;
-    if (softmax_mode == MIATTN_SOFTMAX_FIXED_MAX_CENTERED) {
-      kbar = (float*)(ws + align_up(bh * kMaxSplit * sizeof(float)));
-      part_sum = (float*)((char*)kbar + align_up(bh * d * sizeof(float)));
-    }
-    const int nsplit = kstat_splits(Nk);
+    const bool centred = softmax_mode == MIATTN_SOFTMAX_FIXED_MAX_CENTERED;
     miattn::KStatParams kp{};
     kp.k = k; kp.k_sb = sk.b; kp.k_ss = sk.s; kp.k_sh = sk.h;
     kp.B = B; kp.Hkv = Hkv; kp.Nk = Nk;
-    kp.nsplit = nsplit;
-    kp.keys_per_split = (Nk + nsplit - 1) / nsplit;
-    kp.part_sum = part_sum; kp.part_max = part_max; kp.kbar = kbar;
-    if (miattn::launch_kstats(kp, d, dtype == MIATTN_BF16,
-                              softmax_mode == MIATTN_SOFTMAX_FIXED_MAX_CENTERED, s) != hipSuccess)
+    kp.kb_size = fw.kb_size; kp.nkb = fw.nkb;
+    kp.pmax = (float*)(ws + fw.pmax);
+    kp.radius = centred ? (float*)(ws + fw.radius) : nullptr;
+    kp.centre = centred ? (__bf16*)(ws + fw.centre) : nullptr;
+    if (miattn::launch_kstats(kp, d, dtype == MIATTN_BF16, centred, s) != hipSuccess)
       return MIATTN_ERR_HIP;
-    p.ks.part_max = part_max;
-    p.ks.kbar = kbar;
-    p.ks.nsplit = nsplit;
-    p.ks.keys_per_split = kp.keys_per_split;
+    p.ks.pmax = kp.pmax;
+    p.ks.radius = kp.radius;
+    p.ks.centre = kp.centre;
+    p.ks.kb_size = fw.kb_size;
+    p.ks.nkb = fw.nkb;
+    p.ks.flags = (uint8_t*)(ws + fw.flags);
   }
 
   hipError_t e = dtype == MIATTN_BF16 ? miattn::launch_fwd_bf16(p, d, causal, block, s)

@@ -24,6 +24,10 @@ constexpr float kNegInf = -__builtin_inff();
 // Fixed-max eligibility: the row max may sit at most this many nats below
 // the bound (so every row normaliser stays >= exp(-kTau) >> FLT_MIN).
 constexpr float kTau = 64.0f;
+// ... and the row must see at least this many keys (one key tile): with
+// fewer, the fixed max saves nothing and its bound leaves every weight of the
+// row, the largest included, rounded to bf16 for the P V product.
+constexpr int kMinFixedKeys = 64;
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 

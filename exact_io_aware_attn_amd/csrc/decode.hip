@@ -59,10 +59,19 @@ __device__ __forceinline__ int64_t owner(int64_t x, int64_t T, int64_t S) {
   return ((x + 1) * S - 1) / T;
 }
 
-// Sum of seqlens[0..n) by one wave (every lane gets the result).
-__device__ int64_t wave_sum_lens(const int32_t* seqlens, int n, int lane) {
+// The lengths live on the device and cannot be checked on the host: each is
+// read through this clamp to [0, max_len], so a length outside that range
+// reads no row outside the sequence's cache (a longer one acts as max_len, a
+// negative one as 0). Both kernels see the same clamped lengths.
+__device__ __forceinline__ int seq_len(const int32_t* seqlens, int b, int max_len) {
+  return min(max(seqlens[b], 0), max_len);
+}
+
+// Sum of the clamped lengths of sequences [0, n) by one wave (every lane gets
+// the result).
+__device__ int64_t wave_sum_lens(const int32_t* seqlens, int n, int max_len, int lane) {
   int64_t s = 0;
-  for (int i = lane; i < n; i += 64) s += seqlens[i];
+  for (int i = lane; i < n; i += 64) s += seq_len(seqlens, i, max_len);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
   return s;
@@ -92,7 +101,7 @@ __global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) decode_split_ke
   __bf16* const sk = sKall + wave * SL * D;
   __bf16* const sv = sVall + wave * SL * D;
 
-  const int64_t T = wave_sum_lens(p.seqlens, p.B, lane);
+  const int64_t T = wave_sum_lens(p.seqlens, p.B, p.max_len, lane);
   if (T == 0) return;
   const int64_t S = p.n_splits < T ? p.n_splits : T;
   const int64_t wg = blockIdx.x;
@@ -113,7 +122,7 @@ __global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) decode_split_ke
   // walk the sequences in order; [start, start + len) is sequence b's rows
   int64_t start = 0;
   for (int b = 0; b < p.B && start < hi; ++b) {
-    const int len = p.seqlens[b];
+    const int len = seq_len(p.seqlens, b, p.max_len);
     const int64_t end = start + len;
     if (len > 0 && end > lo) {
       const int k_begin = (int)((lo > start ? lo : start) - start);
@@ -294,9 +303,9 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(const DecodeParams p) 
   const int rows = p.nt * p.Hq;
   const int b = bh / rows, th = bh - b * rows;
   const int lane = threadIdx.x;
-  const int64_t T = wave_sum_lens(p.seqlens, p.B, lane);
-  const int64_t start = wave_sum_lens(p.seqlens, b, lane);
-  const int len = p.seqlens[b];
+  const int64_t T = wave_sum_lens(p.seqlens, p.B, p.max_len, lane);
+  const int64_t start = wave_sum_lens(p.seqlens, b, p.max_len, lane);
+  const int len = seq_len(p.seqlens, b, p.max_len);
   float acc[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;

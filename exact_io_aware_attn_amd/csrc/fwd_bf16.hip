@@ -38,21 +38,25 @@
 //  * The softmax scale is folded into the exponent argument (one FMA per
 //    score: exp2(s * scale*log2(e) - m)), and the running max is used lazily:
 //    each 32-key block is exponentiated against the row's current reference
-//    m straight away, and m moves (with the O rescale) only when a lane's
-//    sum of its 16 values exceeds kBlkSumMax, so neither the block max nor
-//    its cross-lane step is on the common path and P stays <= kBlkSumMax.
-//    Any reference gives the same exact result; the final division by l
-//    uses the same reference.
+//    m straight away, and m moves (with the O rescale) only for the rows
+//    whose sum of 16 values in a lane exceeds kBlkSumMax, so neither the
+//    block max nor its cross-lane step is on the common path and P stays
+//    <= kBlkSumMax. Any reference gives the same exact result. O is divided
+//    by the sum of the bf16-rounded weights that went into PV (a row
+//    dominated by one key returns its value row exactly), the LSE uses the
+//    fp32 sum of the unrounded ones.
 //  * Unmasked dense tiles run as three straight-line stages in a fixed
 //    instruction order: S^T of key block 0, then block 1 with block 0's
 //    exps interleaved, PV of block 0 with block 1's exps, PV of block 1 --
 //    the wave's VALU work issues while its own products occupy the pipe.
-//  * Fixed-max softmax (TPU attention guide, 4단계): the per-row bound
-//    M_i = scale*|q_i|*rho replaces the running max, removing the max
-//    reduction and the accumulator rescale; a 32-row group whose bound is too
-//    loose falls back to the running max. O is divided by the sum of the
-//    bf16 weights that went into PV (the bound leaves every weight below 1
-//    and rounded), the LSE by the fp32 sum.
+//  * Fixed-max softmax (TPU attention guide, 4단계): a per-row upper bound
+//    M_i on the logits (Cauchy-Schwarz, over the key blocks the row can see,
+//    optionally around per-block centres) replaces the running max, removing
+//    the max reduction and the accumulator rescale; a row whose bound could
+//    sit more than kTau nats above its max falls back to the running max.
+//  * Every decision that shapes a row's arithmetic (its reference, rescales,
+//    fixed or running max) is taken from that row's own visible scores and
+//    keys, so the values of keys a mask excludes never change its bits.
 //  * Workgroup order: heaviest causal tiles first; the query heads sharing a
 //    KV head land on the same XCD (blockIdx % 8) so K/V are reused in its L2.
 
@@ -91,10 +95,8 @@ __device__ __forceinline__ void map_workgroup(int i, int G, int nX, int& X, int&
 // partial (m, l, O) are merged at the end: half the serial tile chain per
 // row, for problems too small to fill the chip with whole rows.
 //
-// FX: fixed-max mode compiled in. There O is divided by the sum of the bf16
-// weights it was accumulated with (exact for a single visible key, where the
-// bound leaves P well below 1 and its rounding would otherwise show), and
-// the LSE uses the fp32 sum.
+// FX: fixed-max mode compiled in (the bound, the per-row choice and its
+// record in the workspace).
 // HP: the second half of the causal row blocks (the heavier ones) issues one
 // priority step above the first half; used when every workgroup is resident
 // at once, so the kernel ends with the heaviest ones.
@@ -241,10 +243,21 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
     }
   }
 
-  // ---- fixed-max bound for this lane's row, and the group's eligibility
-  bool fixed = false;
+  // ---- fixed-max bound of this lane's row, from the key blocks the row can
+  // see, and the row's choice. A block meets the row if the row sees one of
+  // its keys. A block the row sees whole gives upper = |q| max|k| and lower =
+  // -upper (or, around the block's centre c with radius R, q.c + |q| R and
+  // q.c - |q| R; the dots q.c of 32 blocks at a time on the MFMA, the centres
+  // as the A operand); the block the causal rule cuts gives |q| times the
+  // prefix max of |k| up to the row's last key. M = scale * max upper bounds
+  // every visible logit and scale * max lower lies below the row max, so the
+  // row's normaliser against M is at least exp(-gap): the row takes the fixed
+  // max iff gap <= kTau and it sees at least kMinFixedKeys keys (below that,
+  // the fixed max saves nothing and would round the row's largest weights to
+  // bf16 too). Keys the row cannot see enter neither value.
+  bool fixed_row = false;
   float m_fix = 0.f;  // bound in log2 units
-  if (p.fixed) {
+  if constexpr (FX) {
     float qq = 0.f;
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t)
@@ -255,28 +268,116 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
       }
     qq += shfl_xor(qq, 32);
     const float qn = sqrtf(qq);
-    // rho^2 = max over the key splits of the partial maxima
     const int64_t bh = (int64_t)b * p.Hkv + hkv;
-    // causal: only the key splits the wave's rows can see (those starting at
-    // or before its last visible key) enter the bound, a tighter bound for
-    // the early rows; block masks take every split
-    bool seen = lane < p.ks.nsplit;
-    if (CAUSAL && !BLOCK) seen = seen && lane * p.ks.keys_per_split <= wave_last + p.causal_off;
-    float r2 = seen ? p.ks.part_max[bh * kMaxSplit + lane] : 0.f;
-    r2 = wave_max(r2);
-    const float rho = sqrtf(r2);
-    float qk = 0.f;
-    if (p.fixed == 2) {
-      const float* kb = p.ks.kbar + bh * D + 8 * h;
+    const int KB = p.ks.kb_size, nkb = p.ks.nkb;
+    const int ncand = BLOCK ? sCount : nkb;  // blocks of the live list, or all
+    const float* __restrict__ pm = p.ks.pmax + bh * p.Nk;
+    // last key seen by this lane's row, and by the wave's first and last rows
+    const int ve = CAUSAL ? min(qrow + p.causal_off, p.Nk - 1) : p.Nk - 1;
+    const int ve_lo = CAUSAL ? min(q0 + p.causal_off, p.Nk - 1) : p.Nk - 1;
+    const int ve_hi = CAUSAL ? min(wave_last + p.causal_off, p.Nk - 1) : p.Nk - 1;
+    const int qb = BLOCK ? wave_last / p.block_q : 0;  // the wave's block row
+    float up = kNegInf, lo = kNegInf;
+    int cnt = 0;  // keys the row sees
+    if (p.fixed != 2) {
+      // blocks every row of the wave sees whole: one block per lane
+      float nmax = kNegInf, nmin = __builtin_inff();
+      int call = 0;
+      for (int base = 0; base < ncand; base += 64) {
+        const int ci = base + lane;
+        const bool valid = ci < ncand;
+        const int kb = valid ? (BLOCK ? (int)sLive[ci] : ci) : 0;
+        bool live = valid;
+        if constexpr (BLOCK) live = live && (wave_uniform || ((bits[ci >> 5] >> (ci & 31)) & 1u));
+        const int ks0 = kb * KB, ks1 = min(ks0 + KB, p.Nk) - 1;
+        const bool whole = live && ks1 <= ve_lo;
+        const float n = pm[ks1];
+        nmax = whole ? fmaxf(nmax, n) : nmax;
+        nmin = whole ? fminf(nmin, n) : nmin;
+        call += whole ? ks1 - ks0 + 1 : 0;
+      }
+      nmax = wave_max(nmax);
+      nmin = -wave_max(-nmin);
 #pragma unroll
-      for (int t = 0; t < KSTEPS; ++t)
+      for (int m = 32; m >= 1; m >>= 1) call += __shfl_xor(call, m, 64);
+      cnt = call;
+      if constexpr (CAUSAL) {
+        // blocks the wave's rows see differently (at most three): per row,
+        // the block max if the row sees it whole, else the prefix max
+        const int kb_b = ve_hi / KB;
+        for (int kb = max(0, ve_lo + 1) / KB; kb <= kb_b; ++kb) {
+          const bool live = !BLOCK || p.block_mask[(int64_t)qb * p.nkb + kb] != 0;
+          const int ks0 = kb * KB, ks1 = min(ks0 + KB, p.Nk) - 1;
+          if (live && ks0 <= ve) {
+            const int last = min(ks1, ve);
+            const float n = pm[last];
+            nmax = fmaxf(nmax, n);
+            nmin = fminf(nmin, n);
+            cnt += last - ks0 + 1;
+          }
+        }
+      }
+      if (nmax > kNegInf) {
+        up = qn * nmax;
+        lo = -qn * nmin;
+      }
+    } else {
+      for (int base = 0; base < ncand; base += 32) {
+        // lanes L and L + 32 hold candidate base + L (L < 32): its key block
+        // (or -1 when dead for the wave), its radius, and its centre as the
+        // A operand of the dots
+        const int ci = base + qc;
+        const bool valid = ci < ncand;
+        const int kb = valid ? (BLOCK ? (int)sLive[ci] : ci) : 0;
+        bool live = valid;
+        if constexpr (BLOCK) live = live && (wave_uniform || ((bits[ci >> 5] >> (ci & 31)) & 1u));
+        const float rad = p.ks.radius[bh * nkb + kb];
+        const int info = live ? kb : -1;
+        const __bf16* cp = p.ks.centre + (bh * nkb + kb) * D + 8 * h;
+        f32x16 dots;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qk += bf2f(qf[t][e]) * kb[16 * t + e];
-      qk += shfl_xor(qk, 32);
+        for (int r = 0; r < 16; ++r) dots[r] = 0.f;
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+          const bf16x8 z = {};
+          dots = mfma32(valid ? *(const bf16x8*)(cp + 16 * t) : z, qf[t], dots);
+        }
+        // register r holds candidate base + 8(r/4) + 4h + r%4 for this row
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int src = 8 * (r >> 2) + 4 * h + (r & 3);
+          const int kbr = __shfl(info, src, 64);
+          const float rr = __shfl(rad, src, 64);
+          const int ks0 = kbr * KB, ks1 = min(ks0 + KB, p.Nk) - 1;
+          if (kbr >= 0 && ks1 <= ve) {
+            const float rq = qn * rr;
+            up = fmaxf(up, dots[r] + rq);
+            lo = fmaxf(lo, dots[r] - rq);
+            cnt += ks1 - ks0 + 1;
+          }
+        }
+      }
+      up = fmaxf(up, shfl_xor(up, 32));
+      lo = fmaxf(lo, shfl_xor(lo, 32));
+      cnt += __shfl_xor(cnt, 32, 64);
+      if (CAUSAL && ve >= 0) {
+        // the block the causal rule cuts: the plain bound over its visible keys
+        const int kb = ve / KB;
+        const int ks0 = kb * KB, ks1 = min(ks0 + KB, p.Nk) - 1;
+        const bool live = !BLOCK || p.block_mask[(int64_t)qb * p.nkb + kb] != 0;
+        if (live && ks1 > ve) {
+          const float u = qn * pm[ve];
+          up = fmaxf(up, u);
+          lo = fmaxf(lo, -u);
+          cnt += ve - ks0 + 1;
+        }
+      }
     }
-    m_fix = p.scale * (qk + qn * rho) * kLog2e;
-    const float gap = row_ok ? 2.f * p.scale * qn * rho : 0.f;
-    fixed = __builtin_amdgcn_readfirstlane((int)(wave_max(gap) <= kTau)) != 0;
+    const float gap = p.scale * (up - lo);
+    fixed_row = row_ok && cnt >= kMinFixedKeys && up > kNegInf && gap <= kTau;
+    m_fix = p.scale * up * kLog2e;
+    if (p.ks.flags != nullptr && row_ok && h == 0 && kp == 0)
+      p.ks.flags[((int64_t)b * p.Hq + hq) * p.Nq + qrow] = fixed_row ? 1 : 0;
   }
 
   // ---- staging: instruction j of this wave fills tile rows
@@ -346,18 +447,22 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[mb][r] = 0.f;
-  float m_run = -__FLT_MAX__;  // reference max (log2 units), online mode; none yet
+  // reference of the exponent (log2 units): the row's fixed bound, or the
+  // lazy running max (none yet: -FLT_MAX)
+  float m_run = fixed_row ? m_fix : -__FLT_MAX__;
+  // lanes whose rows keep a running max (all of them outside fixed-max mode)
+  const uint64_t online_lanes = FX ? __ballot(!fixed_row) : ~0ull;
   float l_run = 0.f;      // this lane's partial row sum (half of the keys)
-  float l_rnd = 0.f;      // FX: the same sum over the bf16-rounded weights
-  // FX: add the eight bf16 weights of a PV operand to l_rnd
+  // the same sum over the bf16-rounded weights used in PV, in two partial
+  // sums (two independent chains of dot products)
+  float l_rnd = 0.f, l_rnd_b = 0.f;
+  // add the eight bf16 weights of a PV operand to the partial sums
   auto sum_rounded = [&](const bf16x8& pf) __attribute__((always_inline)) {
-    if constexpr (FX) {
-      const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
-      l_rnd = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), one2, l_rnd, false);
-      l_rnd = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), one2, l_rnd, false);
-      l_rnd = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), one2, l_rnd, false);
-      l_rnd = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), one2, l_rnd, false);
-    }
+    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+    l_rnd = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 0, 1), one2, l_rnd, false);
+    l_rnd_b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 2, 3), one2, l_rnd_b, false);
+    l_rnd = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 4, 5), one2, l_rnd, false);
+    l_rnd_b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf, pf, 6, 7), one2, l_rnd_b, false);
   };
   const float c = p.scale_log2;
 
@@ -471,19 +576,25 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
     // lane's sum of its 16 values exceeds kBlkSumMax (a value above
     // kBlkSumMax/16 appeared, or the row has no reference yet: m = -FLT_MAX
     // sends every finite score to inf) does the wave take the block's exact
-    // max, move m, rescale O and l, and evaluate the block again. Any
-    // reference gives the same exact result, and P stays <= kBlkSumMax.
+    // max and evaluate the block again; the rows whose own sums exceeded move
+    // m and rescale O and l, the others keep m (alpha = 1, the same exps), so
+    // a row's reference depends on its own scores only. Any reference gives
+    // the same exact result, and P stays <= kBlkSumMax. Rows on the fixed max
+    // never move.
     auto settle = [&](const f32x16& sb, f32x16& e, float& lb) __attribute__((always_inline)) {
-      if (!fixed && __ballot(lb > kBlkSumMax)) {
+      if (__ballot(lb > kBlkSumMax) & online_lanes) {
+        const int over = lb > kBlkSumMax;
+        const bool need = !fixed_row && (over | __shfl_xor(over, 32, 64)) != 0;
         float mx = kNegInf;
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sb[r]);
         mx = fmaxf(mx, shfl_xor(mx, 32)) * c;
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = ex2(m_run - m_new);
+        const float m_new = need ? fmaxf(m_run, mx) : m_run;
+        const float alpha = need ? ex2(m_run - m_new) : 1.f;
         m_run = m_new;
         l_run *= alpha;
         l_rnd *= alpha;
+        l_rnd_b *= alpha;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -496,7 +607,7 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
     // one 32-key block of the generic path: exps, lazy check, P in place
     auto softmax_block = [&](int kb) __attribute__((always_inline)) {
       f32x16 e;
-      float lb = exps(s[kb], e, fixed ? m_fix : m_run);
+      float lb = exps(s[kb], e, m_run);
       settle(s[kb], e, lb);
       s[kb] = e;
     };
@@ -609,7 +720,7 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const float m0 = fixed ? m_fix : m_run;
+      const float m0 = m_run;
       SmPipe P0;
 #pragma unroll
       for (int i = 0; i < NK; ++i) {
@@ -644,7 +755,7 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
       else __builtin_amdgcn_s_setprio(1);
       settle(s[0], e0, lb0);
       // ---- stage 2: PV of block 0 with block 1's softmax
-      const float m1 = fixed ? m_fix : m_run;
+      const float m1 = m_run;
       SmPipe P1;
       bf16x8 pf[2];
       pf[0] = cvt8(e0[0], e0[1], e0[2], e0[3], e0[4], e0[5], e0[6], e0[7]);
@@ -718,7 +829,8 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
     }
   }
 
-  float m_ref = fixed ? m_fix : m_run;
+  l_rnd += l_rnd_b;
+  float m_ref = m_run;
   if constexpr (KS > 1) {
     // ---- merge the key shares of each row block: wave rw + RW hands its
     // (m, l, O) to wave rw through LDS (the K/V buffers are free now); the
@@ -754,11 +866,11 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
   // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2
   const float l_tot = l_run + shfl_xor(l_run, 32);
   const bool live = l_tot > 0.f;
-  float inv = live ? 1.f / l_tot : 0.f;
-  if constexpr (FX) {
-    const float r_tot = l_rnd + shfl_xor(l_rnd, 32);
-    inv = live && r_tot > 0.f ? 1.f / r_tot : 0.f;
-  }
+  // O is divided by the sum of the bf16 weights it was accumulated with (a
+  // row dominated by one key then returns that key's value row exactly, the
+  // weight's own rounding cancelling), the LSE uses the fp32 sum
+  const float r_tot = l_rnd + shfl_xor(l_rnd, 32);
+  const float inv = live && r_tot > 0.f ? 1.f / r_tot : 0.f;
   if (row_ok) {
     __bf16* op = (__bf16*)p.o + b * p.o_sb + (int64_t)qrow * p.o_ss + hq * p.o_sh;
 #pragma unroll

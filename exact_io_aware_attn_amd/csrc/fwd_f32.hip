@@ -66,28 +66,58 @@ __global__ void __launch_bounds__(64 * NWF) fwd_f32_kernel(const FwdParams p) {
   const float* kg = (const float*)p.k + b * p.k_sb + hkv * p.k_sh;
   const float* vg = (const float*)p.v + b * p.v_sb + hkv * p.v_sh;
 
-  // fixed-max bound, and eligibility per wave (its RPW rows), the same rule
-  // as the bf16 kernel's
+  // fixed-max bound of the row and its eligibility, the same rule as the bf16
+  // kernel's: over the key blocks the row sees (whole blocks: |q| max|k|, or
+  // q.c +- |q| R around the block centre; a block cut by the causal rule: |q|
+  // times the prefix max of |k| up to the row's last key), eligible iff the
+  // gap between the bound and the lower bound of the row max is <= kTau and
+  // the row sees at least kMinFixedKeys keys
   bool fixed = false;
   float m_fix = 0.f;
   if (p.fixed) {
-    float qq = 0.f, qk = 0.f;
+    float qq = 0.f;
 #pragma unroll
     for (int i = 0; i < DL; ++i) qq += q[i] * q[i];
-    qq = row_sum(qq);
+    const float qn = sqrtf(row_sum(qq));
     const int64_t bk = (int64_t)b * p.Hkv + hkv;
-    float r2 = lane < p.ks.nsplit ? p.ks.part_max[bk * kMaxSplit + lane] : 0.f;
-    r2 = wave_max(r2);
-    const float rho = sqrtf(r2);
-    if (p.fixed == 2) {
+    const int KB = p.ks.kb_size, nkb = p.ks.nkb;
+    const int vis_end = CAUSAL ? min(qrow + p.causal_off, p.Nk - 1) : p.Nk - 1;
+    const int qb = BLOCK ? (row_ok ? qrow : 0) / p.block_q : 0;
+    const float* pm = p.ks.pmax + bk * p.Nk;
+    float up = kNegInf, lo = kNegInf;
+    int cnt = 0;
+    for (int kb = 0; kb < nkb; ++kb) {
+      float dot = 0.f;
+      if (p.fixed == 2) {
+        const __bf16* cp = p.ks.centre + (bk * nkb + kb) * D + d0;
 #pragma unroll
-      for (int i = 0; i < DL; ++i) qk += q[i] * p.ks.kbar[bk * D + d0 + i];
-      qk = row_sum(qk);
+        for (int i = 0; i < DL; ++i) dot = fmaf(q[i], bf2f(cp[i]), dot);
+        dot = row_sum(dot);
+      }
+      const int ks0 = kb * KB, ks1 = min(ks0 + KB, p.Nk) - 1;
+      const bool live = !BLOCK || p.block_mask[(int64_t)qb * p.nkb + kb] != 0;
+      if (!row_ok || !live || ks0 > vis_end) continue;
+      float u, l;
+      cnt += min(ks1, vis_end) - ks0 + 1;
+      if (ks1 > vis_end) {
+        u = qn * pm[vis_end];
+        l = -u;
+      } else if (p.fixed == 2) {
+        const float rq = qn * p.ks.radius[bk * nkb + kb];
+        u = dot + rq;
+        l = dot - rq;
+      } else {
+        u = qn * pm[ks1];
+        l = -u;
+      }
+      up = fmaxf(up, u);
+      lo = fmaxf(lo, l);
     }
-    const float qn = sqrtf(qq);
-    m_fix = p.scale * (qk + qn * rho) * kLog2e;
-    const float gap = row_ok ? 2.f * p.scale * qn * rho : 0.f;
-    fixed = wave_max(gap) <= kTau;
+    const float gap = p.scale * (up - lo);
+    fixed = row_ok && cnt >= kMinFixedKeys && up > kNegInf && gap <= kTau;
+    m_fix = p.scale * up * kLog2e;
+    if (p.ks.flags != nullptr && row_ok && d0 == 0)
+      p.ks.flags[((int64_t)b * p.Hq + hq) * p.Nq + qrow] = fixed ? 1 : 0;
   }
 
   float m_run = kNegInf, l_run = 0.f;

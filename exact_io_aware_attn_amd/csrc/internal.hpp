@@ -6,10 +6,6 @@
 
 namespace miattn {
 
-// Key-statistics pre-pass (fixed-max softmax): per (batch, KV head) the keys
-// are split into at most kMaxSplit ranges; each range reports a partial max
-// of |k|^2 (or |k - kbar|^2) that the attention kernel reduces on load.
-constexpr int kMaxSplit = 64;
 constexpr int kMaxLiveBlocks = 4096;
 
 // Row segments of a block mask with block_q not a multiple of 32 (built by
@@ -20,11 +16,14 @@ struct SegTable {
   const int2* seg;
 };
 
+// Key statistics of the fixed-max softmax (launch_kstats writes them): the
+// keys of each (batch, KV head) are cut into nkb blocks of kb_size keys.
 struct KStats {
-  const float* part_max;  // [B*Hkv][kMaxSplit], max |k|^2 or |k - kbar|^2
-  const float* kbar;      // [B*Hkv][d] mean key (centred mode) or nullptr
-  int nsplit;
-  int keys_per_split;     // split s covers keys [s * keys_per_split, (s + 1) * keys_per_split)
+  const float* pmax;      // [B*Hkv][Nk]: max |k_i| over the block's keys i <= j
+  const __bf16* centre;   // [B*Hkv][nkb][d]: block mean rounded to bf16 (centred mode)
+  const float* radius;    // [B*Hkv][nkb]: max |k_i - centre| over the block (centred mode)
+  int kb_size, nkb;
+  uint8_t* flags;         // [B][Hq][Nq]: 1 if the row took the fixed max, 0 if it fell back
 };
 
 struct FwdParams {
@@ -53,10 +52,10 @@ struct KStatParams {
   const void* k;
   int64_t k_sb, k_ss, k_sh;
   int B, Hkv, Nk;
-  int nsplit, keys_per_split;
-  float* part_sum;   // [B*Hkv][kMaxSplit][d] (centred pass 1)
-  float* part_max;   // [B*Hkv][kMaxSplit]
-  float* kbar;       // [B*Hkv][d]
+  int kb_size, nkb;   // keys per block, blocks per (batch, KV head)
+  float* pmax;        // [B*Hkv][Nk]
+  __bf16* centre;     // [B*Hkv][nkb][d] (centred mode) or nullptr
+  float* radius;      // [B*Hkv][nkb] (centred mode) or nullptr
 };
 
 struct DecodeParams {

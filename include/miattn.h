@@ -55,16 +55,21 @@ enum { MIATTN_BF16 = 0, MIATTN_F32 = 1 };
 /* Mask kinds (bit flags; CAUSAL | BLOCK combines both rules). */
 enum { MIATTN_MASK_NONE = 0, MIATTN_MASK_CAUSAL = 1, MIATTN_MASK_BLOCK = 2 };
 
-/* Softmax evaluation. ONLINE keeps a running row max and rescales ("Online-
- * Softmax"). FIXED_MAX subtracts a per-row upper bound on the logits fixed
- * before the key loop, scale * |q_i| * max_j |k_j| (Cauchy-Schwarz);
- * FIXED_MAX_CENTERED uses scale * (q_i . kbar + |q_i| * max_j |k_j - kbar|)
- * with kbar the mean key ("TPU attention 최적화 실전 가이드", 4단계). Both are
- * checked per group of 32 query rows of one head: every logit of row i lies
- * within 2 * scale * |q_i| * rho below the bound (rho = max|k_j| or
- * max|k_j - kbar|), and a group where that gap could exceed 64 nats falls back
- * to ONLINE, so exp never underflows the row. The result is the same exact
- * attention either way. */
+/* Softmax evaluation ("TPU attention 최적화 실전 가이드", 4단계; "Online-
+ * Softmax"). ONLINE keeps a running row max and rescales. FIXED_MAX subtracts
+ * a per-row upper bound on the row's logits fixed before the key loop, by
+ * Cauchy-Schwarz over the keys the row can see: the keys of each (batch, KV
+ * head) are cut into blocks (the block mask's block_k, else 256 keys); a
+ * block the row sees whole bounds its logits by scale * |q_i| * max |k_j|, a
+ * block the causal rule cuts by the same over the keys the row sees.
+ * FIXED_MAX_CENTERED bounds a whole block by scale * (q_i . c + |q_i| * max
+ * |k_j - c|) around the block's mean key c (rounded to bf16); cut blocks as in
+ * FIXED_MAX. The bound's distance to the row max is at most the gap between
+ * it and the matching lower bound (|q_i| * max|k_j| below zero, or q_i . c -
+ * |q_i| * max|k_j - c|); a row whose gap could exceed 64 nats falls back to
+ * ONLINE, so exp never underflows the row. Every decision is made per row
+ * from the keys that row sees, so keys a mask excludes never change a row's
+ * output bits. The result is the same exact attention in every mode. */
 enum {
   MIATTN_SOFTMAX_ONLINE = 0,
   MIATTN_SOFTMAX_FIXED_MAX = 1,
@@ -77,14 +82,21 @@ typedef struct {
 } miattn_strides;
 
 /* Bytes of device workspace attn_fwd needs for these arguments (the same
- * meaning as in attn_fwd; block_q is read only when mask_kind has BLOCK).
- * Nonzero for the fixed-max modes (per-(batch, KV head) key statistics) and
- * for a BLOCK mask whose block_q is not a multiple of 32 (a table of row
- * segments: runs of block rows with identical mask rows, cut into pieces of
- * at most 32 rows, built on the stream before the attention kernel). Zero
- * otherwise. Returns 0 for negative sizes. */
-size_t attn_fwd_workspace_bytes(int B, int Hkv, int Nq, int Nk, int d, int mask_kind,
-                                int block_q, int softmax_mode);
+ * meaning as in attn_fwd; block_q and block_k are read only when mask_kind has
+ * BLOCK). Zero for ONLINE without a block mask. Returns 0 for negative sizes.
+ * The workspace holds, in this order, each part starting at a multiple of 256
+ * bytes:
+ *  - fixed-max modes: the key statistics, float [B*Hkv][Nk] (prefix maxima
+ *    of |k| within each key block), then the per-row decisions, uint8
+ *    [B][Hq][Nq]: 1 where the row took the fixed max, 0 where it fell back
+ *    to the running max (readable after the call; for inspection and tests);
+ *    centred mode adds float [B*Hkv][nkb] radii and bf16 [B*Hkv][nkb][d]
+ *    block centres (nkb = Nk / block_k, or ceil(Nk / 256) without a mask);
+ *  - a BLOCK mask whose block_q is not a multiple of 32: a table of row
+ *    segments (runs of block rows with identical mask rows, cut into pieces
+ *    of at most 32 rows), built on the stream before the attention kernel. */
+size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int mask_kind,
+                                int block_q, int block_k, int softmax_mode);
 
 /* Prefill / full-sequence attention.
  *
@@ -108,13 +120,17 @@ size_t attn_fwd_workspace_bytes(int B, int Hkv, int Nq, int Nk, int d, int mask_
  * softmax_mode  MIATTN_SOFTMAX_*
  * strides  NULL (packed) or an array of 4: q, k, v, o
  * workspace, workspace_bytes  device scratch of at least
- *        attn_fwd_workspace_bytes(B, Hkv, Nq, Nk, d, mask_kind, block_q,
- *        softmax_mode) bytes (may be NULL / 0 when that is 0); owned by the
+ *        attn_fwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, mask_kind, block_q,
+ *        block_k, softmax_mode) bytes (may be NULL / 0 when that is 0); owned by the
  *        caller, overwritten by the call, free for reuse once the call's work
  *        on the stream has finished
  * stream   hipStream_t
- * A query row with no visible key yields O = 0 and LSE = -inf. Positions a
- * mask excludes never influence the result, whatever their values. */
+ * A query row with no visible key yields O = 0 and LSE = -inf. Finite values
+ * at positions a mask excludes never change a bit of the result, in every
+ * softmax mode. Non-finite ones are never read under a BLOCK mask (dead
+ * blocks) or past Nk; with bf16 inputs a NaN or Inf in V at a key the causal
+ * rule hides from some rows of a 32-row group that sees other keys of the
+ * same 64-key tile reaches those rows as 0 * NaN in the P V product. */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
              int mask_kind, const uint8_t* block_mask, int block_q, int block_k,
@@ -138,8 +154,10 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_len, int d, i
  * q        device, [B, Hq, d] bf16, packed       (read)
  * k_cache, v_cache  device, [B, max_len, Hkv, d] bf16 (read; rows at or past
  *          seqlens[b] are never read)
- * seqlens  device, int32 [B], each in [0, max_len] (precondition, not checked
- *          on the host: the values live on the device)
+ * seqlens  device, int32 [B], each in [0, max_len]. The values live on the
+ *          device, so the host cannot check them; the kernels clamp each to
+ *          [0, max_len] as they read it (a longer length acts as max_len, a
+ *          negative one as 0), so no length reads outside the cache
  * o        device, [B, Hq, d] bf16, packed        (written)
  * lse      device, float [B, Hq] or NULL          (written)
  * dtype    MIATTN_BF16
@@ -194,8 +212,9 @@ int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
  * block_table  device, int32 [B, max_pages]: cached row r of sequence b is
  *          row r % page_size of page block_table[b * max_pages + r / page_size]
  *          (precondition, not checked: entries < num_pages for every row
- *          below seqlens[b])
- * seqlens  device, int32 [B], each in [0, page_size * max_pages]
+ *          below seqlens[b]; the library is not told num_pages)
+ * seqlens  device, int32 [B], each in [0, page_size * max_pages] (clamped
+ *          to that range on the device, as in attn_decode)
  * page_size  a power of two >= 16
  * q, o, lse, n_new, workspace  as in attn_decode_multi (workspace size from
  *          attn_decode_multi_workspace_bytes) */

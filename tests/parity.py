@@ -5,6 +5,20 @@ relative Frobenius <= 5e-3 over the tensor, LSE max-abs <= 1e-3; fp32 inputs --
 O and LSE max-abs <= 1e-5. Rows with no visible key must be exactly O = 0 and
 LSE = -inf on both sides.
 
+Reading of the bf16 max-abs band: it is stated for outputs below 4 in
+magnitude. A bf16 output is itself rounded to the nearest multiple of 2^-7 on
+[1, 2), 2^-6 on [2, 4) and 2^-5 on [4, 8), so its own rounding error is at
+most 0.0039, 0.0078 and 0.0156 there: below |O*| = 4 the band holds whatever
+the kernel does right, from |O*| = 4 up no bf16 result can meet a flat 1e-2.
+There the bound per element is 1e-2 + 2^-8 |O*| (the output's rounding,
+at most 2^-8 |O*|, on top of the band).
+
+Rows dominated by a few keys (inputs built for it: queries x10, keys several
+times longer than the rest) carry, besides the output's rounding, the bf16
+rounding of their few large weights in P (relative 2^-9, weighted by the
+spread of the dominant values): for them (peaked=True) the bound per element
+is 1e-2 + 2^-8 |O*| at every magnitude.
+
 Gradients (bf16 backward): per tensor, relative Frobenius error <= 1e-2 and
 max-abs error <= 2e-2 * max|reference|. Every product consumes bf16 operands
 (Q, K, V, dO as given, P and dS rounded, relative error <= 2^-9 each), D_i is
@@ -28,14 +42,25 @@ def to64(t):
     return np.asarray(t, dtype=np.float64)
 
 
-def check(o_gpu, O_ref, lse_gpu=None, LSE_ref=None, dtype="bf16", where=""):
+def check(o_gpu, O_ref, lse_gpu=None, LSE_ref=None, dtype="bf16", where="", peaked=False):
     tol = TOL[dtype]
     o = to64(o_gpu)
     assert o.shape == O_ref.shape, (o.shape, O_ref.shape)
     assert np.isfinite(o).all(), f"{where}: non-finite output"
     err = np.abs(o - O_ref)
     mx = float(err.max()) if err.size else 0.0
-    assert mx <= tol["o_abs"], f"{where}: O max-abs {mx:.3e} > {tol['o_abs']}"
+    lim = tol["o_abs"]
+    if dtype == "bf16":
+        big = np.abs(O_ref) >= 4.0
+        if peaked:
+            big = np.ones_like(big)
+        lim = tol["o_abs"] + np.where(big, 2.0 ** -8 * np.abs(O_ref), 0.0)
+    over = err - lim
+    if err.size and float(over.max()) > 0:
+        i = np.unravel_index(int(np.argmax(over)), err.shape)
+        raise AssertionError(f"{where}: O error {err[i]:.3e} at {tuple(int(x) for x in i)} "
+                             f"(got {o[i]:.5f}, exact {O_ref[i]:.5f}) exceeds the band; "
+                             f"max-abs {mx:.3e}")
     if tol["o_rel_fro"] is not None and err.size:
         rel = float(np.linalg.norm(o - O_ref) / max(np.linalg.norm(O_ref), 1e-300))
         assert rel <= tol["o_rel_fro"], f"{where}: O rel-Frobenius {rel:.3e} > {tol['o_rel_fro']}"

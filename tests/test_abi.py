@@ -43,18 +43,26 @@ def test_status_strings():
 
 def test_workspace_sizes():
     NONE, CAUSAL, BLOCK = bd.MIATTN_MASK_NONE, bd.MIATTN_MASK_CAUSAL, bd.MIATTN_MASK_BLOCK
-    assert bd.attn_fwd_workspace_bytes(1, 24, 14080, 14080, 128, NONE, 0, 0) == 0
-    assert bd.attn_fwd_workspace_bytes(1, 24, 14080, 14080, 128, CAUSAL, 80, 0) == 0
-    plain = bd.attn_fwd_workspace_bytes(1, 24, 14080, 14080, 128, NONE, 0, 1)
-    centred = bd.attn_fwd_workspace_bytes(1, 24, 14080, 14080, 128, NONE, 0, 2)
-    assert plain >= 24 * 64 * 4 and centred > plain
+    ws = bd.attn_fwd_workspace_bytes
+    assert ws(1, 24, 24, 14080, 14080, 128, NONE, 0, 0, 0) == 0
+    assert ws(1, 24, 24, 14080, 14080, 128, CAUSAL, 80, 80, 0) == 0
+    # fixed max: prefix maxima [B*Hkv][Nk] fp32, then per-row decisions [B][Hq][Nq]
+    plain = ws(1, 24, 24, 14080, 14080, 128, NONE, 0, 0, 1)
+    assert plain >= 24 * 14080 * 4 + 24 * 14080
+    # centred: radii [B*Hkv][nkb] and bf16 centres [B*Hkv][nkb][d], nkb = ceil(Nk/256) = 55
+    centred = ws(1, 24, 24, 14080, 14080, 128, NONE, 0, 0, 2)
+    assert centred >= plain + 24 * 55 * (4 + 2 * 128)
+    # with a block mask the key blocks are the mask's: 176 blocks of 80
+    assert ws(1, 24, 24, 14080, 14080, 128, BLOCK, 80, 80, 2) >= plain + 24 * 176 * (4 + 256)
+    # GQA: decisions per query head, statistics per KV head
+    assert ws(1, 32, 8, 8192, 8192, 128, CAUSAL, 0, 0, 1) >= 8 * 8192 * 4 + 32 * 8192
     # block masks with block_q not a multiple of 32 carry a row-segment table:
     # 176 block rows of 80 -> at most 3 segments each, 8 bytes per segment
-    seg = bd.attn_fwd_workspace_bytes(1, 24, 14080, 14080, 128, BLOCK, 80, 0)
+    seg = ws(1, 24, 24, 14080, 14080, 128, BLOCK, 80, 80, 0)
     assert seg >= 176 + 176 * 3 * 8
-    assert bd.attn_fwd_workspace_bytes(1, 24, 14080, 14080, 128, BLOCK, 64, 0) == 0
-    assert bd.attn_fwd_workspace_bytes(1, 24, 14080, 14080, 128, BLOCK | CAUSAL, 80, 1) >= plain + seg
-    assert bd.attn_fwd_workspace_bytes(-1, 24, 14080, 14080, 128, BLOCK, 80, 1) == 0
+    assert ws(1, 24, 24, 14080, 14080, 128, BLOCK, 64, 64, 0) == 0
+    assert ws(1, 24, 24, 14080, 14080, 128, BLOCK | CAUSAL, 80, 80, 1) >= plain + seg
+    assert ws(-1, 24, 24, 14080, 14080, 128, BLOCK, 80, 80, 1) == 0
     ws = bd.attn_decode_workspace_bytes(64, 32, 8, 32768, 128, 0)
     assert ws >= (4096 + 64) * 32 * 129 * 4
     assert ws == bd.attn_decode_workspace_bytes(64, 32, 8, 100, 128, 17)

@@ -98,20 +98,59 @@ def test_decode_equals_prefill_with_one_query():
 
 
 def test_full_gqa_decode_b64():
-    """The full decode workload on the GPU, checked on sampled sequences: the
-    shortest, the longest and a few more, all 32 query heads each."""
+    """The full decode workload on the GPU (the launch the bench times),
+    checked on every one of the 64 sequences, all 32 query heads each (each
+    sequence's cache slice is copied to the host and widened on its own)."""
     w = WORKLOADS["gqa-decode-b64"]
     seqlens, q, kc, vc = decode_inputs(w.B, w.Hq, w.Hkv, w.Nk, w.d, torch.bfloat16, w.seed,
                                        w.len_lo, w.len_hi, device=DEV)
     o, lse = attn_decode(q, kc, vc, seqlens)
     torch.cuda.synchronize()
     sl = seqlens.cpu().numpy()
-    picks = sorted({int(np.argmin(sl)), int(np.argmax(sl)), 0, w.B - 1, 17, 40})
-    for b in picks:
+    for b in range(w.B):
         n = int(sl[b])
         O, L = oracle.decode(to64(q[b:b + 1]), to64(kc[b:b + 1, :n]), to64(vc[b:b + 1, :n]),
                              np.array([n]), w.scale)
         check(o[b:b + 1], O, lse[b:b + 1], L, where=f"full decode b={b} len={n}")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_lengths_outside_the_cache_are_clamped(paged):
+    """Lengths live on the device and are not checked on the host: a length
+    above the cache size acts as the cache size and a negative one as 0, in
+    both kernels (so no row outside a sequence's cache is read), bitwise equal
+    to the call with the clamped lengths, and against the oracle."""
+    B, Hq, Hkv, max_len, d = 5, 8, 2, 300, 128
+    seqlens, q, kc, vc = decode_inputs(B, Hq, Hkv, max_len, d, torch.bfloat16, seed=23, len_lo=1)
+    bad = torch.tensor([max_len + 1, 10 ** 9, -7, 150, max_len], dtype=torch.int32)
+    good = bad.clamp(0, max_len)
+    if not paged:
+        o1, l1 = attn_decode(q.to(DEV), kc.to(DEV), vc.to(DEV), bad.to(DEV))
+        o2, l2 = attn_decode(q.to(DEV), kc.to(DEV), vc.to(DEV), good.to(DEV))
+    else:
+        page = 64  # max_len = 300 -> 5 pages of 64 per sequence (320 rows)
+        npg = (max_len + page - 1) // page
+        kp = torch.zeros(B * npg, page, Hkv, d, dtype=torch.bfloat16)
+        vp = torch.zeros_like(kp)
+        for b in range(B):
+            for j in range(npg):
+                r = slice(j * page, min(max_len, (j + 1) * page))
+                kp[b * npg + j, : r.stop - r.start] = kc[b, r]
+                vp[b * npg + j, : r.stop - r.start] = vc[b, r]
+        table = torch.arange(B * npg, dtype=torch.int32).view(B, npg)
+        bad_p = bad.clone()
+        bad_p[0] = npg * page + 1  # past page_size * max_pages
+        good = bad_p.clamp(0, npg * page)
+        o1, l1 = attn_decode_paged(q.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), bad_p.to(DEV))
+        o2, l2 = attn_decode_paged(q.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), good.to(DEV))
+        o1, l1, o2, l2 = o1[:, 0], l1[:, 0], o2[:, 0], l2[:, 0]
+        kc = torch.cat([kp.view(B, npg * page, Hkv, d)], 1)
+        vc = torch.cat([vp.view(B, npg * page, Hkv, d)], 1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    O, L = oracle.decode(to64(q), to64(kc), to64(vc), good.numpy(), 1 / math.sqrt(d))
+    check(o1, O, l1, L, where=f"clamped lengths paged={paged}")
+    assert (o1[2].float() == 0).all() and torch.isneginf(l1[2]).all()
 
 
 # ------------------------------------------------------------ several new tokens

@@ -10,10 +10,10 @@ import pytest
 import torch
 
 import oracle
-from exact_io_aware_attn_amd import attn_fwd
+from exact_io_aware_attn_amd import attn_fwd, attn_fwd_workspace_bytes, fixed_max_decisions
 from exact_io_aware_attn_amd.inputs import WORKLOADS, frame_block_mask, prefill_inputs
 
-from parity import check, sample_rows, to64
+from parity import check, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -127,19 +127,26 @@ def test_bf16_fixed_max_shifted_keys_centered():
         check(o, O, lse, L, where=mode)
 
 
-def test_bf16_fixed_max_fallback_with_scaled_queries():
-    """Q x10 makes the bound far too loose (gap > 87 nats): the rule must fall
-    back to the running max, and the result must still meet the band (without
-    the fallback the row sums underflow and LSE is wrong). Q x10 makes each
-    row's softmax nearly one-hot, so O is nearly a single V row; V is scaled
-    by 1/4 to keep |O| in the range the bf16 band is stated for (bf16 rounding
-    of P and of O alone reaches 1e-2 at |O| ~ 4)."""
+@pytest.mark.parametrize("v_scale", [0.25, 1.0])
+@pytest.mark.parametrize("mode", ["online", "fixed_max", "fixed_max_centered"])
+def test_bf16_scaled_queries_peaked_rows(mode, v_scale):
+    """Q x10 makes every row's softmax nearly one-hot, so O is nearly a single
+    V row, and the fixed-max bound far too loose (gap > 87 nats): every row
+    must fall back to the running max, and the result must still be exact
+    (without the fallback the row sums underflow and the LSE is wrong).
+    With V x1/4 |O| stays below 2 and the band applies; with V as drawn |O*|
+    reaches 4 and more, and the bound for rows dominated by a few keys
+    applies (see parity.py).
+    The sum of the rounded weights divides O, so a row dominated by one key
+    adds no error of its own on top of that rounding."""
     q, k, v = prefill_inputs(1, 2, 2, 320, 320, 128, torch.bfloat16, seed=7)
     q = (q.float() * 10).to(torch.bfloat16)
-    v = (v.float() * 0.25).to(torch.bfloat16)
-    o, lse = _run(q, k, v, softmax="fixed_max")
+    v = (v.float() * v_scale).to(torch.bfloat16)
+    o, lse = _run(q, k, v, softmax=mode)
     O, L = _ref(q, k, v, 1 / math.sqrt(128))
-    check(o, O, lse, L, where="fallback")
+    if v_scale == 1:
+        assert np.abs(O).max() > 3.5  # the case is reached
+    check(o, O, lse, L, where=f"peaked {mode}", peaked=v_scale == 1)
 
 
 def test_f32_fixed_max():
@@ -308,18 +315,58 @@ def test_repeatable_bitwise():
 
 
 # ------------------------------------------------------------------ masked positions
-def test_causal_future_keys_are_excluded_bitwise():
-    """Changing keys/values j > t (to other finite values) leaves rows i <= t
-    bit-identical: excluded pairs contribute exactly nothing."""
-    q, k, v = prefill_inputs(1, 2, 2, 256, 256, 128, torch.bfloat16, seed=14)
-    t = 150
+@pytest.mark.parametrize("mode", ["online", "fixed_max", "fixed_max_centered"])
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,t", [
+    (1, 2, 2, 256, 128, 150),     # 4-wave workgroups; row 150 inside a 32-row group
+    (32, 16, 4, 300, 128, 140),   # 8-wave workgroups, GQA
+    (1, 8, 8, 1500, 64, 777),     # d = 64, keys split between two waves
+    (2, 4, 2, 700, 64, 400),      # d = 64, 4-wave workgroups
+])
+def test_causal_future_keys_are_excluded_bitwise(mode, B, Hq, Hkv, N, d, t):
+    """Changing keys/values j > t (to other finite values: keys 8x longer and
+    shifted, so the later rows' bounds, fallbacks and rescales change) leaves
+    rows i <= t bit-identical in every softmax mode: excluded pairs contribute
+    exactly nothing, and every decision a row's arithmetic depends on comes
+    from its own visible keys. In the fixed-max modes rows 0..t keep the
+    fixed max in both runs."""
+    q, k, v = prefill_inputs(B, Hq, Hkv, N, N, d, torch.bfloat16, seed=14 + N + d)
     k2, v2 = k.clone(), v.clone()
-    k2[:, t + 1:] = (k2[:, t + 1:].float() * 3 + 1).to(torch.bfloat16)
+    k2[:, t + 1:] = (k2[:, t + 1:].float() * 8 + 1).to(torch.bfloat16)
     v2[:, t + 1:] = (v2[:, t + 1:].float() * -2 + 5).to(torch.bfloat16)
-    o1, l1 = _run(q, k, v, causal=True)
-    o2, l2 = _run(q, k2, v2, causal=True)
+    ws1, ws2 = _workspace(B, Hq, Hkv, N, N, d, mode), _workspace(B, Hq, Hkv, N, N, d, mode)
+    o1, l1 = _run(q, k, v, causal=True, softmax=mode, workspace=ws1)
+    o2, l2 = _run(q, k2, v2, causal=True, softmax=mode, workspace=ws2)
     assert torch.equal(o1[:, :t + 1], o2[:, :t + 1])
     assert torch.equal(l1[:, :, :t + 1], l2[:, :, :t + 1])
+    if mode != "online":
+        f1 = fixed_max_decisions(ws1, B, Hq, Hkv, N, N)
+        f2 = fixed_max_decisions(ws2, B, Hq, Hkv, N, N)
+        m = oracle.MIN_KEYS - 1  # rows before it see less than one key tile
+        assert torch.equal(f1[:, :, :t + 1], f2[:, :, :t + 1])
+        assert bool((f1[:, :, m:t + 1] == 1).all()) and bool((f1[:, :, :m] == 0).all())
+        assert bool((f2[:, :, t + 1:] == 0).any())  # the longer keys moved later rows
+
+
+def check_decisions(flags, q, k, mode, margin=0.05, **mask):
+    """The kernel's per-row choice (fixed max or fallback) against the oracle's
+    eligibility rule (fixed_max_bounds): equal on every row whose gap lies
+    more than `margin` nats from tau (float32 sums may decide the rest either
+    way; they must be few)."""
+    M, gap, el = oracle.fixed_max_bounds(to64(q), to64(k), 1 / math.sqrt(q.shape[-1]),
+                                         centered=mode == "fixed_max_centered", **mask)
+    flags = np.asarray(flags)
+    assert flags.shape == el.shape
+    assert set(np.unique(flags)) <= {0, 1}
+    clear = ~(np.abs(np.nan_to_num(gap, nan=np.inf) - oracle.TAU) <= margin)
+    assert clear.mean() > 0.99
+    bad = np.argwhere(((flags == 1) != el) & clear)
+    assert bad.size == 0, f"{len(bad)} decisions differ, first {bad[:5].tolist()}"
+
+
+def _workspace(B, Hq, Hkv, Nq, Nk, d, mode, mask_kind=1, bq=0, bk=0):
+    from exact_io_aware_attn_amd.binding import SOFTMAX_MODES
+    n = attn_fwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, mask_kind, bq, bk, SOFTMAX_MODES[mode])
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=DEV)
 
 
 @pytest.mark.parametrize("frames,flen,blk,heads,g", [
@@ -328,28 +375,33 @@ def test_causal_future_keys_are_excluded_bitwise():
     (16, 880, 80, 2, 7),     # the video shape, 4-wave workgroups
     (16, 880, 80, 24, 7),    # the video shape, 8-wave workgroups
 ])
-@pytest.mark.parametrize("mode", ["online", "fixed_max"])
-def test_dead_block_nan_never_read(mode, frames, flen, blk, heads, g):
-    """NaN in the keys/values of key frame g: queries whose frames do not
-    attend it are bit-identical to the clean run and finite, including block
-    rows (80, 48) that are not a multiple of 32 rows.
-
-    The fixed-max bound is a per-head statistic over all keys, so the frame's
-    keys are scaled down in both runs: they never set max |k|, and NaN rows
-    are ignored by that max, so the bound is the same in both runs."""
+@pytest.mark.parametrize("mode", ["online", "fixed_max", "fixed_max_centered"])
+@pytest.mark.parametrize("poison", ["nan", "long_keys"])
+def test_dead_block_nan_never_read(mode, poison, frames, flen, blk, heads, g):
+    """Key frame g gets NaN keys/values, or finite keys 3x longer (and shifted)
+    with other values: queries whose frames do not attend it are
+    bit-identical to the clean run and finite, in every softmax mode,
+    including block rows (80, 48) that are not a multiple of 32 rows. The
+    fixed-max bound of a row comes from the key blocks it sees, so the
+    frame's keys never enter the bound of a frame that does not attend it."""
     n = frames * flen
     bm = frame_block_mask(frames, flen, blk)
     q, k, v = prefill_inputs(1, heads, heads, n, n, 128, torch.bfloat16, seed=15)
-    k[:, g * flen:(g + 1) * flen] = (k[:, g * flen:(g + 1) * flen].float() * 0.25).to(torch.bfloat16)
     o1, l1 = _run(q, k, v, block_mask=bm, block=(blk, blk), softmax=mode)
     k2, v2 = k.clone(), v.clone()
-    k2[:, g * flen:(g + 1) * flen] = float("nan")
-    v2[:, g * flen:(g + 1) * flen] = float("nan")
+    fr = slice(g * flen, (g + 1) * flen)
+    if poison == "nan":
+        k2[:, fr] = float("nan")
+        v2[:, fr] = float("nan")
+    else:
+        k2[:, fr] = (k2[:, fr].float() * 3 + 0.5).to(torch.bfloat16)
+        v2[:, fr] = (v2[:, fr].float() * -2 + 3).to(torch.bfloat16)
     o2, l2 = _run(q, k2, v2, block_mask=bm, block=(blk, blk), softmax=mode)
     for f in range(frames):
         rows = slice(f * flen, (f + 1) * flen)
-        if abs(f - g) <= 1:
-            assert torch.isnan(o2[:, rows].float()).any(), f  # frame f attends g
+        if abs(f - g) <= 1 or g == 0:
+            if poison == "nan":
+                assert torch.isnan(o2[:, rows].float()).any(), f  # frame f attends g
             continue
         assert torch.equal(o1[:, rows], o2[:, rows]), f
         assert torch.equal(l1[:, :, rows], l2[:, :, rows]), f
@@ -357,57 +409,76 @@ def test_dead_block_nan_never_read(mode, frames, flen, blk, heads, g):
 
 
 # ------------------------------------------------------------------ full-size workloads
-def _full(name, mode="online", rows_per_head=None, heads=None):
+def _full(name, mode="online", heads=None):
+    """The workload at its full size, in the launch configuration the bench
+    times, against the oracle on every row of the given query heads (all by
+    default); in the fixed-max modes the per-row decisions against the
+    oracle's rule as well."""
     w = WORKLOADS[name]
-    ins = {}
     q, k, v = prefill_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, torch.bfloat16, w.seed, device=DEV)
     bm = frame_block_mask(w.frames, w.frame_len, w.block) if w.frames else None
     kw = dict(causal=w.causal, softmax=mode)
+    mask = dict(causal=w.causal)
     if bm is not None:
         kw.update(block_mask=bm, block=(w.block, w.block))
-    o, lse = attn_fwd(q, k, v, **kw)
+        mask.update(block_mask=bm, block_q=w.block, block_k=w.block)
+    kind = (1 if w.causal else 0) | (2 if bm is not None else 0)
+    ws = _workspace(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, mode, kind, w.block, w.block)
+    o, lse = attn_fwd(q, k, v, workspace=ws, **kw)
     torch.cuda.synchronize()
-    bounds = list(range(w.frame_len, w.Nq, w.frame_len)) if w.frames else []
-    rows = sample_rows(w.Nq, boundaries=bounds, seed=w.seed)
     heads = list(range(w.Hq)) if heads is None else heads
-    ok = dict(block_mask=bm, block_q=w.block or None, block_k=w.block or None) if bm is not None else {}
-    rt = torch.as_tensor(rows, device=DEV)
     ht = torch.as_tensor(heads, device=DEV)
     for b in range(w.B):
-        O, L = oracle.attention(to64(q[b:b + 1]), to64(k[b:b + 1]), to64(v[b:b + 1]), w.scale,
-                                causal=w.causal, heads=heads, rows=rows, **ok)
-        check(o[b:b + 1][:, rt][:, :, ht], O, lse[b:b + 1][:, ht][:, :, rt], L,
-              where=f"{name} {mode} b={b}")
+        qb, kb, vb = to64(q[b:b + 1]), to64(k[b:b + 1]), to64(v[b:b + 1])
+        O, L = oracle.attention(qb, kb, vb, w.scale, heads=heads, **mask)
+        check(o[b:b + 1][:, :, ht], O, lse[b:b + 1][:, ht], L, where=f"{name} {mode} b={b}")
+    if mode != "online":
+        f = fixed_max_decisions(ws, w.B, w.Hq, w.Hkv, w.Nq, w.Nk)[:, ht].cpu().numpy()
+        # the oracle's rule over the same heads, each with its own KV head
+        g = w.Hq // w.Hkv
+        ks = k.cpu()[:, :, [h // g for h in heads]]
+        check_decisions(f, q[:, :, ht].cpu(), ks, mode, **mask)
 
 
 def test_full_gpt2_causal():
-    _full("gpt2-causal", heads=[0, 5, 11])
+    _full("gpt2-causal")
 
 
 def test_full_gpt2_medium_causal():
-    _full("gpt2-medium-causal", heads=[0, 9, 15])
+    _full("gpt2-medium-causal")
 
 
 def test_full_llama3_8b_gqa_causal():
-    _full("llama3-8b-gqa-causal-8k", heads=[0, 3, 4, 17, 31])
+    _full("llama3-8b-gqa-causal-8k")
 
 
-@pytest.mark.parametrize("mode", ["online", "fixed_max"])
+@pytest.mark.parametrize("mode", ["online", "fixed_max", "fixed_max_centered"])
 def test_full_video_frames(mode):
-    _full("video-frames-16x880", mode=mode, heads=[0, 13, 23])
+    _full("video-frames-16x880", mode=mode, heads=[0, 3, 6, 9, 12, 15, 19, 23])
+
+
+@pytest.mark.parametrize("mode", ["fixed_max", "fixed_max_centered"])
+def test_full_llama3_8b_gqa_causal_fixed_max(mode):
+    _full("llama3-8b-gqa-causal-8k", mode=mode, heads=[0, 1, 2, 3, 17, 30, 31])
 
 
 @pytest.mark.parametrize("mode", ["fixed_max", "fixed_max_centered"])
 def test_bf16_fixed_max_causal_large_late_keys(mode):
-    # the last 64 keys are 3x longer: with a bound over every key the early
-    # 32-row groups' gap (about 2 scale |q| max|k| = 84 nats) exceeds the 64-nat
-    # limit; under the causal rule only the last rows see those keys, so the
-    # bound over the splits a wave can see keeps the early groups eligible.
-    # Their values are shrunk so the peaked last rows keep outputs of moderate
-    # size (the bf16 rounding of a large output would dominate the error).
-    q, k, v = prefill_inputs(2, 4, 2, 700, 700, 128, torch.bfloat16, seed=77)
-    k[:, -64:] = (k[:, -64:].float() * 3).to(torch.bfloat16)
-    v[:, -64:] = (v[:, -64:].float() * 0.25).to(torch.bfloat16)
-    o, lse = _run(q, k, v, causal=True, softmax=mode)
+    """The last 64 keys are 8x longer: a bound over every key would put the
+    early rows' gap near 100 nats, past the 64-nat limit; under the causal
+    rule only the last rows see those keys, so the bound over the key blocks
+    each row sees keeps the earlier rows (from the first one that sees a whole
+    key tile) on the fixed max and sends the last ones back to the running
+    max, each as the oracle's rule decides. The last rows are dominated by a
+    few keys: the bound for such rows applies."""
+    B, Hq, Hkv, N = 2, 4, 2, 700
+    q, k, v = prefill_inputs(B, Hq, Hkv, N, N, 128, torch.bfloat16, seed=77)
+    k[:, -64:] = (k[:, -64:].float() * 8).to(torch.bfloat16)
+    ws = _workspace(B, Hq, Hkv, N, N, 128, mode)
+    o, lse = _run(q, k, v, causal=True, softmax=mode, workspace=ws)
     O, L = _ref(q, k, v, 1 / math.sqrt(128), causal=True)
-    check(o, O, lse, L, where=f"{mode} causal large late keys")
+    check(o, O, lse, L, where=f"{mode} causal large late keys", peaked=True)
+    f = fixed_max_decisions(ws, B, Hq, Hkv, N, N).cpu().numpy()
+    assert (f[:, :, oracle.MIN_KEYS - 1:N - 64] == 1).all()
+    assert (f[:, :, N - 64:] == 0).mean() > 0.5
+    check_decisions(f, q, k, mode, causal=True)

@@ -466,10 +466,16 @@ def test_scaled_queries_are_ineligible_and_would_underflow():
     assert (M[0, 1] - S.max(-1)).max() > 87.4  # exp(-gap) would be below the fp32 minimum normal
 
 
-def test_rows_without_keys_are_ineligible():
+def test_rows_without_keys_or_with_few_keys_are_ineligible():
     q, k = _randn(1, 10, 1, 8), _randn(1, 4, 1, 8)
-    M, gap, el = oracle.fixed_max_bounds(q, k, 0.5, causal=True)   # rows 0..5 see nothing
+    M, gap, el = oracle.fixed_max_bounds(q, k, 0.5, causal=True, min_keys=1)  # rows 0..5 see nothing
     assert np.isneginf(M[0, 0, :6]).all() and not el[0, 0, :6].any() and el[0, 0, 6:].all()
+    # rows 6..9 see 1..4 keys: below the default minimum of one key tile
+    _, _, el = oracle.fixed_max_bounds(q, k, 0.5, causal=True)
+    assert not el.any()
+    q, k = _randn(1, 100, 1, 8), _randn(1, 100, 1, 8)
+    _, _, el = oracle.fixed_max_bounds(q, k, 0.05, causal=True)
+    assert not el[0, 0, :oracle.MIN_KEYS - 1].any() and el[0, 0, oracle.MIN_KEYS - 1:].all()
 
 
 def test_round_to_bf16_matches_torch():
