@@ -33,11 +33,14 @@ torch autograd in float64 on the CPU (tests/test_oracle_backward.py).
 
 Parity unpinned: the eligibility threshold ``TAU`` = 64 is a constant chosen
 here from an underflow argument, not a value the pages give; only the rule's
-soundness (the normaliser stays far above the fp32 minimum) is tested.
+soundness (the normaliser stays far above the fp32 minimum) is tested. The
+same holds for ``MIN_KEYS`` = 64, the fewest visible keys for which a row
+takes the fixed max.
 """
 
 from .backward import attention_backward  # noqa: F401
 from .attention import (  # noqa: F401
+    MIN_KEYS,
     TAU,
     attention,
     decode,

@@ -27,6 +27,9 @@ import numpy as np
 # Eligibility threshold for the fixed-max softmax, in nats. Parity unpinned:
 # chosen here, not given by the pages (see fixed_max_bounds).
 TAU = 64.0
+# ... and a row must see at least this many keys to take the fixed max
+# (parity unpinned as well; see fixed_max_bounds).
+MIN_KEYS = 64
 
 _ROW_CHUNK = 2048
 
@@ -193,7 +196,7 @@ def round_to_bf16(x):
 
 
 def fixed_max_bounds(q, k, scale, *, centered=False, causal=False, block_mask=None,
-                     block_q=None, block_k=None, key_block=256, tau=TAU):
+                     block_q=None, block_k=None, key_block=256, tau=TAU, min_keys=MIN_KEYS):
     """Per-row fixed reference M_i, its gap and eligibility, from the keys the
     row can see (TPU attention guide, 4단계).
 
@@ -222,9 +225,12 @@ def fixed_max_bounds(q, k, scale, *, centered=False, causal=False, block_mask=No
     least scale * lower, so the row's max logit is at least scale * max_b lower.
     gap_i = M_i - scale * max_b lower bounds how far the row max sits below
     M_i, the row's normaliser against M_i is at least exp(-gap_i), and the row
-    is eligible iff it sees a key and gap_i <= tau (then that normaliser stays
-    far above the float32 minimum normal exp(-87.3)). Parity unpinned: tau
-    (default 64 nats) is chosen here.
+    is eligible iff gap_i <= tau (then that normaliser stays far above the
+    float32 minimum normal exp(-87.3)) and the row sees at least min_keys keys
+    (a row with fewer gains nothing from a fixed reference, and with it every
+    weight of the row, its largest included, would be rounded to the
+    precision of the P V product). Parity unpinned: tau (default 64 nats) and
+    min_keys (default 64, one key tile) are chosen here.
 
     Returns (M, gap, eligible), each [B, Hq, Nq]; rows that see no key get
     M = -inf, gap = nan, eligible = False.
@@ -273,12 +279,14 @@ def fixed_max_bounds(q, k, scale, *, centered=False, causal=False, block_mask=No
                     up = np.where(meets, up, -np.inf).max(-1)
                     lo = np.where(meets, lo, -np.inf).max(-1)
                     live = meets.any(-1)
+                    nseen = allowed.sum(-1)
                     Mi = np.where(live, scale * up, -np.inf)
                     with np.errstate(invalid="ignore"):
                         gi = np.where(live, scale * (up - lo), np.nan)
                     M[b, h, rows] = Mi
                     gap[b, h, rows] = gi
-                    elig[b, h, rows] = live & (np.nan_to_num(gi, nan=np.inf) <= tau)
+                    elig[b, h, rows] = (live & (nseen >= min_keys)
+                                        & (np.nan_to_num(gi, nan=np.inf) <= tau))
     return M, gap, elig
 
 
