@@ -11,7 +11,7 @@ _BINDING_NAMES = ("attn_fwd", "attn_decode", "attn_decode_multi", "attn_bwd", "p
                   "prepare_decode_paged",
                   "attn_decode_multi_workspace_bytes", "attn_fwd_workspace_bytes", "attn_decode_workspace_bytes",
                   "attn_bwd_workspace_bytes",
-                  "attn_status_str", "library", "MiattnError", "fixed_max_decisions")
+                  "attn_status_str", "library", "MiattnError", "fixed_max_decisions", "attn_decode_noalloc")
 
 
 def __getattr__(name):

@@ -21,7 +21,7 @@ MIATTN_BF16, MIATTN_F32 = 0, 1
 MIATTN_MASK_NONE, MIATTN_MASK_CAUSAL, MIATTN_MASK_BLOCK = 0, 1, 2
 SOFTMAX_MODES = {"online": 0, "fixed_max": 1, "fixed_max_centered": 2}
 
-_EXPORTS = ("attn_fwd", "attn_fwd_workspace_bytes", "attn_decode",
+_EXPORTS = ("attn_fwd", "attn_fwd_workspace_bytes", "attn_decode", "attn_decode_noalloc",
             "attn_decode_workspace_bytes", "attn_decode_multi",
             "attn_decode_multi_workspace_bytes", "attn_decode_paged", "attn_bwd",
             "attn_bwd_workspace_bytes",
@@ -62,6 +62,9 @@ def library():
     lib.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I,
                                 ctypes.POINTER(_Strides), P, Z, P]
     lib.attn_decode.restype = I
+    lib.attn_decode_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I,
+                                        ctypes.POINTER(_Strides), P]
+    lib.attn_decode_noalloc.restype = I
     lib.attn_decode_multi_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.attn_decode_multi_workspace_bytes.restype = Z
     lib.attn_decode_multi.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, I,
@@ -258,6 +261,31 @@ def attn_decode(q, k_cache, v_cache, seqlens, *, scale=None, kv_splits=0, return
     rc = library().attn_decode(*args)
     if rc != 0:
         raise MiattnError(rc, "attn_decode")
+    return o, lse
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, seqlens, o, lse=None, *, scale=None, kv_splits=0):
+    """attn_decode through the entry point that allocates nothing: the caller
+    passes the outputs o [B,Hq,d] bf16 and (optionally) lse [B,Hq] fp32; the
+    split-K partials go to the library's static per-device scratch. q must be
+    contiguous [B,Hq,d] and seqlens contiguous int32 [B]. Nothing is allocated
+    here either. Returns (o, lse)."""
+    _check_gpu(q, k_cache, v_cache, seqlens, o)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B,Hq,d]; caches [B,max_len,Hkv,d]")
+    if not q.is_contiguous() or not o.is_contiguous() or not seqlens.is_contiguous():
+        raise ValueError("q, o and seqlens must be contiguous")
+    if seqlens.dtype != torch.int32:
+        raise TypeError("seqlens must be int32")
+    B, Hq, d = q.shape
+    _, max_len, Hkv, _ = k_cache.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = (_Strides * 2)(_strides4(k_cache), _strides4(v_cache))
+    rc = library().attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens),
+                                       _ptr(o), _ptr(lse), _dtype_code(q), B, Hq, Hkv, max_len,
+                                       d, scale, kv_splits, st, _stream(q.device))
+    if rc != 0:
+        raise MiattnError(rc, "attn_decode_noalloc")
     return o, lse
 
 

@@ -8,6 +8,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "internal.hpp"
 
@@ -235,12 +236,39 @@ size_t attn_decode_multi_workspace_bytes(int B, int n_new, int Hq, int Hkv, int 
 
 namespace {
 
+// ---- the allocation-free decode's scratch (attn_decode_noalloc): one static
+// array per device, holding the split-K partials of the last such call
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of the current device's copy of `scratch`, looked up
+// once per device with that device current (each device holds its own copy
+// at its own address; the array's name in host code is only a stand-in).
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MIATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return MIATTN_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MIATTN_OK;
+}
+
+// noalloc: the partials go to the device's static scratch, sized for the
+// split count actually used instead of the largest one
 int decode_impl(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* seqlens, void* o, float* lse, int dtype, int B, int nt, int Hq,
                 int Hkv, int max_len, int d, float scale, int kv_splits,
                 const miattn_strides* cache_strides, void* workspace, size_t workspace_bytes,
                 void* stream, const int32_t* table = nullptr, int page_size = 0,
-                int max_pages = 0) {
+                int max_pages = 0, bool noalloc = false) {
   if (dtype != MIATTN_BF16) return MIATTN_ERR_UNSUPPORTED;
   if (B < 0 || nt <= 0 || Hq <= 0 || Hkv <= 0 || max_len < 0 || d <= 0) return MIATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return MIATTN_ERR_SHAPE;
@@ -269,8 +297,18 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
     return MIATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return MIATTN_ERR_UNSUPPORTED;
 
-  const size_t need = decode_ws(B, Hq * nt, d);
-  const size_t po = align_up((size_t)(miattn::kMaxSplits + B) * Hq * nt * d * sizeof(float));
+  const int n_splits = decode_splits(Hkv, kv_splits);
+  size_t need = decode_ws(B, Hq * nt, d);
+  size_t po = align_up((size_t)(miattn::kMaxSplits + B) * Hq * nt * d * sizeof(float));
+  if (noalloc) {
+    const size_t slots = (size_t)(n_splits + B) * Hq * nt;
+    po = align_up(slots * d * sizeof(float));
+    need = po + align_up(slots * sizeof(float));
+    if (need > kNoAllocScratchBytes) return MIATTN_ERR_WORKSPACE;
+    const int rc = noalloc_scratch(&workspace);
+    if (rc != MIATTN_OK) return rc;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   if (workspace == nullptr || workspace_bytes < need) return MIATTN_ERR_WORKSPACE;
 
   miattn::DecodeParams p{};
@@ -283,7 +321,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   while (paged && (1 << p.page_shift) < page_size) ++p.page_shift;
   p.max_pages = max_pages;
   p.scale_log2 = scale * 1.4426950408889634f;
-  p.n_splits = decode_splits(Hkv, kv_splits);
+  p.n_splits = n_splits;
   p.part_o = (float*)workspace;
   p.part_lse = (float*)((char*)workspace + po);
   hipError_t e = miattn::launch_decode(p, d, (hipStream_t)stream);
@@ -315,6 +353,14 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 void* stream) {
   return decode_impl(q, k_cache, v_cache, seqlens, o, lse, dtype, B, 1, Hq, Hkv, max_len, d, scale,
                      kv_splits, cache_strides, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seqlens, void* o, float* lse, int dtype, int B, int Hq,
+                        int Hkv, int max_len, int d, float scale, int kv_splits,
+                        const miattn_strides* cache_strides, void* stream) {
+  return decode_impl(q, k_cache, v_cache, seqlens, o, lse, dtype, B, 1, Hq, Hkv, max_len, d, scale,
+                     kv_splits, cache_strides, nullptr, 0, stream, nullptr, 0, 0, true);
 }
 
 int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,

@@ -13,7 +13,8 @@
  * Conventions common to every entry point
  *  - Pointers marked "device" are HIP device pointers; the caller owns them.
  *    The library allocates nothing, frees nothing and keeps no mutable global
- *    state, so calls on different streams may run concurrently.
+ *    state, so calls on different streams may run concurrently -- except
+ *    attn_decode_noalloc, whose calls share a static scratch per device.
  *  - Layout is [batch, seq, heads, d] ("Multi-Query Attention (MQA)",
  *    "Comparison"), d contiguous (stride 1). Other strides are given in
  *    elements through miattn_strides; NULL means packed.
@@ -172,6 +173,27 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 int Hq, int Hkv, int max_len, int d, float scale, int kv_splits,
                 const miattn_strides* cache_strides, void* workspace,
                 size_t workspace_bytes, void* stream);
+
+/* attn_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Same arguments, meaning and result as attn_decode
+ * (bitwise equal to it for the same kv_splits); the split-K partials go to a
+ * static 32 MiB array in the library's device code, one per device, held
+ * until the process ends. The call allocates nothing (no hipMalloc, no
+ * allocating library routine); on its first call on a device it looks up that
+ * device's copy of the array (the device must be current, as for any launch
+ * on `stream`). The partials take (S + B) * Hq * (d + 1) * 4 bytes (each of
+ * the two parts rounded up to 256 bytes), with S = kv_splits or the automatic
+ * count (eight 64-lane waves per CU of the device; 256 ranges on 256 CUs for
+ * Hkv = 8); a call that needs more than 32 MiB returns MIATTN_ERR_WORKSPACE
+ * and launches nothing. Every call on a device shares that device's array:
+ * calls that overlap on one device (on different streams, or from different
+ * threads without ordering) race and may return wrong results; calls ordered
+ * on one stream are safe, since each call writes every partial it reads. */
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seqlens, void* o, float* lse, int dtype, int B, int Hq,
+                        int Hkv, int max_len, int d, float scale, int kv_splits,
+                        const miattn_strides* cache_strides, void* stream);
 
 /* Bytes of device workspace attn_decode_multi needs (0 when the sizes are
  * invalid). Independent of max_len and kv_splits. */

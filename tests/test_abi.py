@@ -125,6 +125,29 @@ def test_decode_validation(kw, status):
     assert _dec(**kw) == status
 
 
+def _dec_noalloc(**kw):
+    a = dict(q=16, k=16, v=16, seqlens=16, o=16, lse=None, dtype=0, B=2, Hq=8, Hkv=2,
+             max_len=256, d=128, scale=0.1, chunk=0)
+    a.update(kw)
+    P = ctypes.c_void_p
+    return bd.library().attn_decode_noalloc(P(a["q"]), P(a["k"]), P(a["v"]), P(a["seqlens"]),
+                                            P(a["o"]), P(a["lse"]), a["dtype"], a["B"], a["Hq"],
+                                            a["Hkv"], a["max_len"], a["d"], a["scale"], a["chunk"],
+                                            None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=1), 3), (dict(d=80), 3), (dict(Hq=7), 2), (dict(scale=-1.0), 6),
+    (dict(chunk=-1), 6), (dict(seqlens=None), 1), (dict(B=0), 0),
+    # partials past the 32 MiB static scratch: (4096 + 64) slots x 32 heads x 129 floats
+    (dict(B=64, Hq=32, Hkv=8, chunk=4096), 4),
+])
+def test_decode_noalloc_validation(kw, status):
+    """The allocation-free decode validates like attn_decode (no workspace
+    argument) and refuses partials beyond its static scratch, all on the host."""
+    assert _dec_noalloc(**kw) == status
+
+
 def test_bwd_workspace_size():
     # two fp32 rows of Nq rounded up to 64 per (batch, query head)
     assert bd.attn_bwd_workspace_bytes(2, 4, 100) == 2 * 2 * 4 * 128 * 4
