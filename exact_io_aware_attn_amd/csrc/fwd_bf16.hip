@@ -685,8 +685,21 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
       f32x16 x, e;
       float l0, l1;
     };
-    auto sm_chunk = [&](SmPipe& P, const f32x16& sb, float m, int j) __attribute__((always_inline)) {
+    // MK: the element rule on this tile (causal diagonal or key tail): value i
+    // of a lane's block sits at key 8(i/4) + i%4 past the lane's first key of
+    // the block and is kept iff that offset is <= lim; otherwise the score
+    // itself becomes -inf (in place, so the rare rescale, which takes the
+    // block max and evaluates the block again from the scores, sees it too)
+    auto sm_chunk = [&](SmPipe& P, f32x16& sb, float m, int j, auto mkc, int lim)
+                        __attribute__((always_inline)) {
+      constexpr bool MK = decltype(mkc)::value;
       if (j < 8) {
+        if constexpr (MK) {
+          const int k0 = 8 * ((2 * j) >> 2) + ((2 * j) & 3);
+          const int k1 = 8 * ((2 * j + 1) >> 2) + ((2 * j + 1) & 3);
+          sb[2 * j] = k0 <= lim ? sb[2 * j] : kNegInf;
+          sb[2 * j + 1] = k1 <= lim ? sb[2 * j + 1] : kNegInf;
+        }
         P.x[2 * j] = __builtin_fmaf(sb[2 * j], c, -m);
         P.x[2 * j + 1] = __builtin_fmaf(sb[2 * j + 1], c, -m);
       }
@@ -706,7 +719,16 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
     // The wave's issue priority falls as it moves through the tile (2, 1, 0
     // by stage): of the two waves sharing a SIMD, the one further behind is
     // served first, so they reach the tile's barrier closer together.
-    auto body_fast = [&]() __attribute__((always_inline)) {
+    auto body_fast = [&](auto mkc) __attribute__((always_inline)) {
+      // masked tiles (dense masks only): the last key this lane's row may
+      // see, as an offset from the lane's first key of block 0
+      int lim0 = 0;
+      if constexpr (decltype(mkc)::value && !BLOCK) {
+        int last = p.Nk - 1;
+        if (CAUSAL) last = min(last, qrow + p.causal_off);
+        lim0 = last - tile_k0 - 4 * h;
+      }
+      const int lim1 = lim0 - 32;
       if (HP && prio) __builtin_amdgcn_s_setprio(3);
       else __builtin_amdgcn_s_setprio(2);
       // ---- stage 1: S^T block 0, then block 1 with block 0's softmax
@@ -730,10 +752,10 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
         const int j0 = i - KSTEPS - 1;
         if (j0 >= 0) {
           if constexpr (KSTEPS == 8) {
-            sm_chunk(P0, s[0], m0, j0);
+            sm_chunk(P0, s[0], m0, j0, mkc, lim0);
           } else {
-            sm_chunk(P0, s[0], m0, 2 * j0);
-            sm_chunk(P0, s[0], m0, 2 * j0 + 1);
+            sm_chunk(P0, s[0], m0, 2 * j0, mkc, lim0);
+            sm_chunk(P0, s[0], m0, 2 * j0 + 1, mkc, lim0);
           }
         }
         fence();
@@ -742,7 +764,7 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
       {
         constexpr int done = KSTEPS == 8 ? KSTEPS - 1 : 2 * (KSTEPS - 1);
 #pragma unroll
-        for (int j = done; j < 10; ++j) sm_chunk(P0, s[0], m0, j);
+        for (int j = done; j < 10; ++j) sm_chunk(P0, s[0], m0, j, mkc, lim0);
       }
       constexpr int VLEAD = 3;  // V fragments in flight
       bf16x8 vf[NPV];
@@ -770,17 +792,17 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
         oacc[j % MB] = mfma32(vf[j], pf[j / MB], oacc[j % MB]);
         if (j + VLEAD < NPV) vf[j + VLEAD] = vfrag((j + VLEAD) / MB, (j + VLEAD) % MB);
         if constexpr (NPV == 8) {
-          sm_chunk(P1, s[1], m1, j);
+          sm_chunk(P1, s[1], m1, j, mkc, lim1);
         } else {
-          sm_chunk(P1, s[1], m1, 2 * j);
-          sm_chunk(P1, s[1], m1, 2 * j + 1);
+          sm_chunk(P1, s[1], m1, 2 * j, mkc, lim1);
+          sm_chunk(P1, s[1], m1, 2 * j + 1, mkc, lim1);
         }
         fence();
       }
       {
         constexpr int done = NPV == 8 ? NPV : 2 * NPV;
 #pragma unroll
-        for (int j = done; j < 10; ++j) sm_chunk(P1, s[1], m1, j);
+        for (int j = done; j < 10; ++j) sm_chunk(P1, s[1], m1, j, mkc, lim1);
       }
 #pragma unroll
       for (int j = 0; j < VLEAD; ++j) vf[j] = vfrag(2 + j / MB, j % MB);
@@ -806,8 +828,14 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
       }
     };
     // state 1 has every key group live (and no causal rule), dense or block
-    if (state == 1) body_fast();
-    else if (state == 2) body(std::true_type());
+    // dense masks: tiles that cross the causal diagonal or hold the key tail
+    // take the same fixed-order body with the element rule folded into the
+    // exponent step; block masks with partly live tiles take the plain path
+    if (state == 1) body_fast(std::false_type());
+    else if (state == 2) {
+      if constexpr (!BLOCK) body_fast(std::true_type());
+      else body(std::true_type());
+    }
   };
 
   const int n_steps = (n_tiles + KS - 1) / KS;
