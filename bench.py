@@ -13,7 +13,11 @@ Printed (one JSON line):
   value      prefill forward throughput, TFLOP/s of algorithmic work
              (4 d per attended query-key pair) over the prefill part of the steps
   decode     KV-read GB/s of the decode part (sum of lengths x Hkv x d x 2 x 2 B)
-  roofline   prefill kernel against the dense bf16 MFMA peak
+  roofline   prefill kernel against the dense bf16 MFMA peak (and against that peak
+             scaled to the kernel's sustained engine clock)
+  clock      the main kernel's sustained engine clock, from a counter pass of the
+             same bench command (GRBM_GUI_ACTIVE per XCD over the kernel's time),
+             stored in profiles/clock.json with a hash of the kernel sources
   roofline_decode  decode against the HBM peak
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample
   ms_parts_back_to_back  per part, the average of --back-to-back calls (200)
@@ -50,6 +54,10 @@ HBM_PEAK = 8000.0         # GB/s
 # stored with them and are reported only while those sources are unchanged.
 DEFAULT = ("llama3-8b-gqa-causal-8k", "gqa-decode-b64")   # the default step
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+TRAFFIC_NOTE = ("stored, not measured in this run: HBM bytes per launch from two rocprofv3 "
+                "counter passes (FETCH_SIZE, WRITE_SIZE, scaled by a plain copy) kept in "
+                "profiles/hbm_traffic.json; null whenever the kernel sources no longer match "
+                "the hash stored with them")
 
 
 def measured_traffic(part):
@@ -66,6 +74,34 @@ def measured_traffic(part):
     if h.hexdigest()[:16] != rec["source_sha256_16"]:
         return None
     return rec["bytes"]
+
+
+CLOCK_FILE = os.path.join(ROOT, "profiles", "clock.json")
+
+
+def _sources_match(rec):
+    import hashlib
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        with open(os.path.join(ROOT, "exact_io_aware_attn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16] == rec["source_sha256_16"]
+
+
+def stored_clock(workload):
+    """The main kernel's sustained engine clock for this workload, from the
+    stored counter pass, or None (no record, or the sources changed since)."""
+    try:
+        rec = json.load(open(CLOCK_FILE))[workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    if not _sources_match(rec):
+        return None
+    return {"mhz": rec["mhz"], "kernel": rec["kernel"],
+            "source": "stored, not measured in this run: GRBM_GUI_ACTIVE / 8 XCDs over the "
+                      "kernel's duration in a rocprofv3 counter pass of the same bench command "
+                      "(profiles/clock.json); null whenever the kernel sources no longer match "
+                      "the hash stored with it"}
 
 
 def parse():
@@ -304,13 +340,15 @@ def main():
         out.update(value=tflops, unit="TFLOP/s")
         roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
                 "frac": tflops / peak,
-                "traffic": measured_traffic("prefill") if main_p.name == DEFAULT[0] else None}
+                "traffic": measured_traffic("prefill") if main_p.name == DEFAULT[0] else None,
+                "traffic_source": TRAFFIC_NOTE}
     else:
         gbs = main_p.bytes / (ms_avg[0] * 1e-3) / 1e9
         out.update(value=gbs, unit="GB/s")
         roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK, "unit": "GB/s",
                 "frac": gbs / HBM_PEAK,
-                "traffic": measured_traffic("decode") if main_p.name == DEFAULT[1] else None}
+                "traffic": measured_traffic("decode") if main_p.name == DEFAULT[1] else None,
+                "traffic_source": TRAFFIC_NOTE}
     out.update(n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=ms_step,
                higher_is_better=True, scaling="weak", vs_baseline=None,
                dtype="bf16" if main_p.w.dtype == "bf16" else "f32",
@@ -327,6 +365,13 @@ def main():
     out["ms_parts_median"] = {p.name: sorted(m)[len(m) // 2] for p, m in zip(parts, ms)}
     out["ms_parts_min"] = {p.name: min(m) for p, m in zip(parts, ms)}
     out["ms_parts_back_to_back"] = b2b
+    clk = stored_clock(main_p.name)
+    out["clock"] = clk
+    if clk is not None and roof["bound"] == "mfma":
+        # the same peak at the engine clock the kernel held (the 2516.6 TFLOP/s
+        # figure assumes 2.4 GHz)
+        roof["peak_at_sustained_clock"] = roof["peak"] * clk["mhz"] / 2400.0
+        roof["frac_at_sustained_clock"] = roof["achieved"] / roof["peak_at_sustained_clock"]
     out["roofline"] = roof
     if len(parts) > 1 and parts[1].kind == "decode":
         d = parts[1]
@@ -334,7 +379,8 @@ def main():
         out["decode"] = {"value": gbs, "unit": "GB/s", "ms": ms_avg[1]}
         out["roofline_decode"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK,
                                   "unit": "GB/s", "frac": gbs / HBM_PEAK,
-                                  "traffic": measured_traffic("decode")}
+                                  "traffic": measured_traffic("decode"),
+                                  "traffic_source": TRAFFIC_NOTE}
     if not args.no_cpu_baseline and main_p.kind == "prefill":
         out["cpu_baseline"] = cpu_baseline(main_p, args.cpu_seconds)
     elif not args.no_cpu_baseline and main_p.kind == "backward":
