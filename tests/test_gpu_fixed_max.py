@@ -7,7 +7,7 @@ that never does. The kernel records each row's choice in its workspace
 oracle.fixed_max_bounds ("TPU attention 최적화 실전 가이드", 4단계: the bound, its
 gap to the row max, and the fallback of loose rows) on inputs that are all
 eligible (N(0,1)), all ineligible (Q x10) and mixed (Q x10 on some heads; keys
-3x longer in one part of the sequence, which only some rows see), in every
+8x longer in one part of the sequence, which only some rows see), in every
 kernel configuration: 4- and 8-wave workgroups, keys split between two
 waves, block masks with and without row segments, and the fp32 kernel.
 Outputs are checked against the oracle too.
