@@ -91,6 +91,10 @@ def _fwd(**kw):
     # block_q not a multiple of 32: the row-segment table needs workspace
     (dict(mask_kind=2, block_mask=16, block_q=16, block_k=16), 4),
     (dict(B=0), 0), (dict(Nq=0), 0),
+    # limits: at most 4096 key blocks per mask row; one (batch, KV head) of K
+    # or V under 2 GiB (32-bit row offsets)
+    (dict(mask_kind=2, block_mask=16, block_q=16, block_k=16, Nk=16 * 4097), 3),
+    (dict(Nk=1 << 23), 3),
 ])
 def test_fwd_validation(kw, status):
     """Each of these returns before anything is enqueued (no GPU needed)."""
@@ -179,6 +183,12 @@ def _bwd(**kw):
     (dict(q=18), 3), (dict(dv=24), 3),
     (dict(ws=None), 4), (dict(ws_bytes=100), 4),
     (dict(B=0), 0), (dict(Nq=0, Nk=0), 0),
+    # limits: at most 4096 streamed 64-row tiles per side under a block mask;
+    # one (batch, head) of Q, dO, K or V under 2 GiB (32-bit offsets)
+    (dict(mask_kind=2, block_mask=16, block_q=16, block_k=16, Nq=64 * 4097), 3),
+    (dict(mask_kind=2, block_mask=16, block_q=16, block_k=16, Nk=64 * 4097), 3),
+    (dict(mask_kind=0, Nk=1 << 23), 3),
+    (dict(mask_kind=0, Nq=1 << 22), 3),
 ])
 def test_bwd_validation(kw, status):
     """Each of these returns before anything is enqueued (no GPU needed)."""
