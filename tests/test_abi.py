@@ -241,3 +241,28 @@ def _decp(**kw):
 ])
 def test_decode_paged_validation(kw, status):
     assert _decp(**kw) == status
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built HIP library every entry point raises; there is no
+    other implementation to fall back on."""
+    import torch
+    monkeypatch.setattr(bd, "_lib", None)
+    monkeypatch.setattr(bd, "LIB_PATH", str(tmp_path / "libmiattn.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        bd.library()
+    q = torch.zeros(1, 64, 2, 64, dtype=torch.bfloat16)
+    kv = torch.zeros(1, 64, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises((RuntimeError, ValueError)):
+        bd.attn_fwd(q, kv, kv)
+
+
+def test_product_code_does_not_use_the_oracle():
+    """The package (binding, inputs, build, kernels) never imports or names
+    the oracle package."""
+    import pathlib
+    import re
+    root = pathlib.Path(bd.__file__).parent
+    pat = re.compile(r"^\s*(import|from)\s+oracle\b|\boracle\.", re.M)
+    for f in list(root.rglob("*.py")) + list(root.rglob("*.hip")) + list(root.rglob("*.cpp")):
+        assert not pat.search(f.read_text()), f
