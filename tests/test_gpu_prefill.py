@@ -1,7 +1,8 @@
 """attn_fwd on the GPU against the fp64 oracle (element by element).
 
 Small cases span several 128-row query tiles and 64-key tiles with ragged
-tails; full-size workloads are checked on sampled rows and heads."""
+tails; the full-size workloads are checked on every row (of every head, or
+of eight heads for the video workload); 65536-key sequences on sampled rows."""
 
 import math
 
@@ -13,7 +14,7 @@ import oracle
 from exact_io_aware_attn_amd import attn_fwd, attn_fwd_workspace_bytes, fixed_max_decisions
 from exact_io_aware_attn_amd.inputs import WORKLOADS, frame_block_mask, prefill_inputs
 
-from parity import check, to64
+from parity import check, sample_rows, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -460,6 +461,29 @@ def test_full_video_frames(mode):
 @pytest.mark.parametrize("mode", ["fixed_max", "fixed_max_centered"])
 def test_full_llama3_8b_gqa_causal_fixed_max(mode):
     _full("llama3-8b-gqa-causal-8k", mode=mode, heads=[0, 1, 2, 3, 17, 30, 31])
+
+
+@pytest.mark.parametrize("mode", ["online", "fixed_max"])
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d", [
+    (1, 2, 1, 65536, 65536, 128),   # 8-wave workgroups, 1024 key tiles per late row
+    (1, 4, 2, 700, 65573, 64),      # a short query block at the end of a ragged long key range
+])
+def test_long_sequence_sampled_rows(mode, B, Hq, Hkv, Nq, Nk, d):
+    """Causal prefill over 65536 keys: sampled rows (tile edges, first and last,
+    random) against the oracle, each row given exactly the keys the causal
+    rule lets it see (the row alone as the query, keys 0 .. i + Nk - Nq, no
+    mask), so no N x N reference is formed."""
+    q, k, v = prefill_inputs(B, Hq, Hkv, Nq, Nk, d, torch.bfloat16, seed=Nq + d, device=DEV)
+    ws = _workspace(B, Hq, Hkv, Nq, Nk, d, mode, 1)
+    o, lse = attn_fwd(q, k, v, causal=True, softmax=mode, workspace=ws)
+    torch.cuda.synchronize()
+    qc, kc, vc, oc, lc = (t.cpu() for t in (q, k, v, o, lse))
+    scale = 1 / math.sqrt(d)
+    for r in sample_rows(Nq, tile=256, extra=12, seed=d):
+        last = r + Nk - Nq
+        O, L = oracle.attention(to64(qc[:, r:r + 1]), to64(kc[:, :last + 1]), to64(vc[:, :last + 1]),
+                                scale)
+        check(oc[:, r:r + 1], O, lc[:, :, r:r + 1], L, where=f"{mode} Nq={Nq} Nk={Nk} row {r}")
 
 
 @pytest.mark.parametrize("mode", ["fixed_max", "fixed_max_centered"])
