@@ -88,7 +88,8 @@ def attention(q, k, v, scale, *, causal=False, block_mask=None, block_q=None,
     3. Disallowed pairs get -inf, so they contribute exactly 0 below.
     4. m = row max of S; P = exp(S - m); l = row sum of P; P = P / l
        (the safe softmax of "FlashAttention / Tiling" and "Online-Softmax").
-    5. O = P V; LSE = m + ln l (natural log of the row's normaliser over the
+    5. O = P V over the allowed keys only (an Inf or NaN value at a key the row
+       cannot see is no term of its sum); LSE = m + ln l (natural log of the row's normaliser over the
        scaled scores, the statistic kept for the backward pass, FlashAttention
        explainer §4 재계산).
     A row with no allowed key returns O = 0 and LSE = -inf.
@@ -127,7 +128,20 @@ def attention(q, k, v, scale, *, causal=False, block_mask=None, block_q=None,
                 l = P.sum(axis=1)
                 l_safe = np.where(live, l, 1.0)
                 Pn = P / l_safe[:, None]
-                O[b, r0:r0 + rr.size, hi, :] = np.where(live[:, None], Pn @ Vb, 0.0)
+                fin = np.isfinite(Vb)
+                if fin.all():
+                    PV = Pn @ Vb
+                else:
+                    # the sum runs over allowed keys only: a value the row
+                    # cannot see is no term of its output (0 * NaN would be).
+                    # Finite values through the product (their masked
+                    # weights are exact zeros), then each Inf/NaN added to
+                    # the rows allowed to see its key
+                    PV = Pn @ np.where(fin, Vb, 0.0)
+                    for j, dc in zip(*np.nonzero(~fin)):
+                        a = allowed[:, j]
+                        PV[a, dc] += Pn[a, j] * Vb[j, dc]
+                O[b, r0:r0 + rr.size, hi, :] = np.where(live[:, None], PV, 0.0)
                 LSE[b, hi, r0:r0 + rr.size] = np.where(live, m_safe + np.log(l_safe), -np.inf)
     return O, LSE
 

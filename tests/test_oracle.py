@@ -521,3 +521,43 @@ def test_brute_force_tiny():
                 o = sum(e[a] / z * v[0, keys[a], g, t] for a in range(len(keys)))
                 assert abs(O[0, i, h, t] - o) < 1e-12
             assert abs(L[0, h, i] - (mx + math.log(z))) < 1e-12
+
+
+def test_values_a_row_cannot_see_are_no_term_of_its_output():
+    """An Inf or NaN in V at a key the mask hides from a row leaves that row
+    exactly as with a finite value there; rows that see the key propagate it
+    (IEEE). Causal (with Nq != Nk), block mask, and decode past the length."""
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((1, 12, 2, 8))
+    k = rng.standard_normal((1, 15, 1, 8))
+    v = rng.standard_normal((1, 15, 1, 8))
+    off = 15 - 12
+    for bad in (np.nan, np.inf):
+        vb = v.copy()
+        vb[0, 9, 0, :] = bad
+        O0, L0 = oracle.attention(q, k, v, 0.3, causal=True)
+        O1, L1 = oracle.attention(q, k, vb, 0.3, causal=True)
+        sees = np.arange(12) + off >= 9
+        assert np.array_equal(O1[0, ~sees], O0[0, ~sees])
+        assert not np.isfinite(O1[0, sees]).any()
+        assert np.array_equal(L1, L0)
+    bm = np.array([[1, 0, 1], [0, 1, 1], [1, 1, 0]], dtype=np.uint8)
+    q3 = rng.standard_normal((1, 12, 1, 8))
+    k3 = rng.standard_normal((1, 15, 1, 8))
+    v3 = rng.standard_normal((1, 15, 1, 8))
+    v3b = v3.copy()
+    v3b[0, 7, 0, 2] = np.nan  # key block 1: seen by block rows 1 and 2
+    O0, _ = oracle.attention(q3, k3, v3, 0.5, block_mask=bm, block_q=4, block_k=5)
+    O1, _ = oracle.attention(q3, k3, v3b, 0.5, block_mask=bm, block_q=4, block_k=5)
+    rows = np.arange(12) // 4 >= 1
+    assert np.array_equal(O1[0, ~rows], O0[0, ~rows])
+    assert np.isnan(O1[0, rows, 0, 2]).all() and np.isfinite(O1[0, rows][..., [0, 1, 3]]).all()
+    seqlens = np.array([5, 9])
+    qd = rng.standard_normal((2, 2, 8))
+    kc = rng.standard_normal((2, 12, 1, 8))
+    vc = rng.standard_normal((2, 12, 1, 8))
+    vcb = vc.copy()
+    vcb[0, 5:] = np.nan
+    vcb[1, 9:] = np.inf
+    assert np.array_equal(oracle.decode(qd, kc, vcb, seqlens, 0.4)[0],
+                          oracle.decode(qd, kc, vc, seqlens, 0.4)[0])
