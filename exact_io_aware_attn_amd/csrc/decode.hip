@@ -281,17 +281,82 @@ __global__ void __launch_bounds__(NW * 64, NW >= 4 ? 8 / NW : 1) decode_split_ke
       float l_tot = l_run;
       l_tot += shfl_xor(l_tot, 16);
       l_tot += shfl_xor(l_tot, 32);
+      // several new tokens: the product for a slice serves tokens that see a
+      // key and tokens that do not, so an Inf or NaN at such a key can reach
+      // the latter through a zero weight. A row whose accumulators are not all
+      // finite hands the merge a NaN LSE instead, and the merge recomputes it
+      int nf = 0;
+      if (p.nt > 1) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) nf |= !__builtin_isfinite(oacc[mb][r]);
+        nf |= __shfl_xor(nf, 16, 64);  // the row's four lanes: n + 16 g4
+        nf |= __shfl_xor(nf, 32, 64);
+      }
       if (n < G * p.nt) {
         const int64_t row = ((wg + b) * p.nt + tok) * p.Hq + hkv * G + hg;
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         float* po = p.part_o + row * D + 4 * g4;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) *(f32x4*)(po + 16 * mb) = oacc[mb] * inv;
-        if (g4 == 0) p.part_lse[row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
+        if (g4 == 0)
+          p.part_lse[row] = nf ? __builtin_nanf("") : l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
       }
     }
     start = end;
   }
+}
+
+// Exact recompute of one row (batch b, token and query head th) over all its
+// visible cache rows, for rows a range flagged (see the split kernel): keys
+// one at a time with a running max, lanes holding d / 64 columns each, every
+// excluded key skipped. A cold path.
+template <int D>
+__device__ __forceinline__ void merge_exact_row(const DecodeParams& p, int b, int th,
+                                                          int len) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x;
+  const int tok = th / p.Hq, hq = th - tok * p.Hq;
+  const int hkv = hq / (p.Hq / p.Hkv);
+  const int k_lim = min(len, len - p.nt + tok + 1);
+  const int64_t bh = ((int64_t)b * p.nt + tok) * p.Hq + hq;
+  const __bf16* qr = (const __bf16*)p.q + bh * D;
+  const __bf16* kb = (const __bf16*)p.kc + hkv * p.k_sh;
+  const __bf16* vb = (const __bf16*)p.vc + hkv * p.v_sh;
+  const int pmask = (1 << p.page_shift) - 1;
+  float qv[PER], acc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    qv[j] = bf2f(qr[lane + 64 * j]);
+    acc[j] = 0.f;
+  }
+  float mx = kNegInf, l = 0.f;
+  for (int key = 0; key < k_lim; ++key) {
+    int64_t ko = (int64_t)b * p.k_sb + (int64_t)key * p.k_ss;
+    int64_t vo = (int64_t)b * p.v_sb + (int64_t)key * p.v_ss;
+    if (p.table != nullptr) {
+      const int64_t page = p.table[(int64_t)b * p.max_pages + (key >> p.page_shift)];
+      ko = page * p.k_sb + (int64_t)(key & pmask) * p.k_ss;
+      vo = page * p.v_sb + (int64_t)(key & pmask) * p.v_ss;
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) dot = __builtin_fmaf(qv[j], bf2f(kb[ko + lane + 64 * j]), dot);
+    const float sc = wave_sum(dot) * p.scale_log2;
+    const float m_new = fmaxf(mx, sc);
+    const float alpha = ex2(mx - m_new);
+    const float pw = ex2(sc - m_new);
+    l = l * alpha + pw;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] = __builtin_fmaf(pw, bf2f(vb[vo + lane + 64 * j]), acc[j] * alpha);
+    mx = m_new;
+  }
+  const bool live = k_lim > 0;
+  __bf16* o = (__bf16*)p.o + bh * D;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) o[lane + 64 * j] = (__bf16)(live ? acc[j] / l : 0.f);
+  if (p.lse != nullptr && lane == 0) p.lse[bh] = live ? (mx + log2f(l)) * kLn2 : kNegInf;
 }
 
 // One workgroup (a single wave) per (batch, new token, query head): merge the
@@ -313,7 +378,16 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(const DecodeParams p) 
   if (len > 0) {
     const int64_t S = p.n_splits < T ? p.n_splits : T;
     const int64_t i0 = owner(start, T, S), i1 = owner(start + len - 1, T, S);
-    for (int64_t i = i0; i <= i1; ++i) M = fmaxf(M, p.part_lse[(i + b) * rows + th]);
+    bool redo = false;  // a partial flagged non-finite (NaN LSE)
+    for (int64_t i = i0; i <= i1; ++i) {
+      const float x = p.part_lse[(i + b) * rows + th];
+      redo |= x != x;
+      M = fmaxf(M, x);
+    }
+    if (redo) {
+      merge_exact_row<D>(p, b, th, len);
+      return;
+    }
     const float Mu = M == kNegInf ? 0.f : M;
     for (int64_t i = i0; i <= i1; ++i) {
       const int64_t row = (i + b) * rows + th;

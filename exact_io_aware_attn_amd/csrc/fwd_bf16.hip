@@ -90,6 +90,79 @@ __device__ __forceinline__ void map_workgroup(int i, int G, int nX, int& X, int&
   }
 }
 
+// Exact recompute of one wave's rows (a cold path, taken only when the
+// wave's accumulators hold an Inf or NaN, which a value at a key the causal
+// rule hides from some of its rows can cause: the matrix product multiplies
+// it by a zero weight). Row qc of lane (qc, h) is q0 + qc; the two lanes of a
+// row hold halves of d. Keys are visited one at a time with a running max, every
+// excluded pair skipped, so a non-finite value reaches exactly the rows that
+// see its key; O and the LSE written by the main path are overwritten.
+// Not inlined, so its registers do not add to the tile loop's.
+template <int D, bool CAUSAL, bool BLOCK>
+__device__ __attribute__((noinline)) void exact_rows(
+    const __bf16* __restrict__ qb, const __bf16* __restrict__ kb, const __bf16* __restrict__ vb,
+    __bf16* __restrict__ ob, float* __restrict__ lse_row, int64_t q_ss, int64_t k_ss,
+    int64_t v_ss, int64_t o_ss, int Nq, int Nk, int causal_off, float scale_log2,
+    const uint8_t* __restrict__ block_mask, int block_q, int block_k, int nkb, int q0, int nrows) {
+  constexpr int DH = D / 2;
+  const int lane = threadIdx.x & 63;
+  const int qc = lane & 31, h = lane >> 5;
+  const int row = q0 + qc;
+  const bool ok = qc < nrows && row < Nq;
+  const int r = ok ? row : q0;
+  float qv[DH], o[DH];
+#pragma unroll
+  for (int t = 0; t < DH; t += 8) {
+    const bf16x8 x = *(const bf16x8*)(qb + (int64_t)r * q_ss + h * DH + t);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qv[t + e] = bf2f(x[e]);
+      o[t + e] = 0.f;
+    }
+  }
+  int last = Nk - 1;
+  if (CAUSAL) last = min(last, r + causal_off);
+  if (!ok) last = -1;
+  int last_w = last;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) last_w = max(last_w, __shfl_xor(last_w, m, 64));
+  float mx = kNegInf, l = 0.f;
+  for (int j = 0; j <= last_w; ++j) {
+    bool vis = j <= last;
+    if (BLOCK) vis = vis && block_mask[(int64_t)(r / block_q) * nkb + j / block_k] != 0;
+    float dot = 0.f;
+#pragma unroll
+    for (int t = 0; t < DH; t += 8) {
+      const bf16x8 x = *(const bf16x8*)(kb + (int64_t)j * k_ss + h * DH + t);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qv[t + e], bf2f(x[e]), dot);
+    }
+    dot += shfl_xor(dot, 32);
+    if (vis) {
+      const float sc = dot * scale_log2;
+      const float m_new = fmaxf(mx, sc);
+      const float alpha = ex2(mx - m_new);
+      const float pw = ex2(sc - m_new);
+      l = l * alpha + pw;
+#pragma unroll
+      for (int t = 0; t < DH; t += 8) {
+        const bf16x8 x = *(const bf16x8*)(vb + (int64_t)j * v_ss + h * DH + t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[t + e] = __builtin_fmaf(pw, bf2f(x[e]), o[t + e] * alpha);
+      }
+      mx = m_new;
+    }
+  }
+  if (!ok) return;
+  const bool live = last >= 0 && (l > 0.f || l != l);
+  const float inv = live ? 1.f / l : 0.f;
+#pragma unroll
+  for (int t = 0; t < DH; t += 4)
+    *(bf16x4*)(ob + (int64_t)row * o_ss + h * DH + t) =
+        cvt4(o[t] * inv, o[t + 1] * inv, o[t + 2] * inv, o[t + 3] * inv);
+  if (lse_row != nullptr && h == 0) lse_row[row] = live ? (mx + log2f(l)) * kLn2 : kNegInf;
+}
+
 // NW waves per workgroup (4 or 8), 32 query rows per wave. KS = 2 splits
 // the keys of each 32-row block between two waves (alternate tiles), whose
 // partial (m, l, O) are merged at the end: half the serial tile chain per
@@ -911,6 +984,24 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
       }
     if (p.lse != nullptr && h == 0)
       p.lse[((int64_t)b * p.Hq + hq) * p.Nq + qrow] = live ? (m_ref + log2f(l_tot)) * kLn2 : kNegInf;
+  }
+  // Under the causal rule one product serves rows that see a key and rows
+  // that do not, so an Inf or NaN in V at such a key reaches the latter
+  // through a zero weight. A non-finite accumulator is the only trace it can
+  // leave: such a wave recomputes its rows exactly (a cold path, also taken
+  // by rows whose own visible keys hold Inf or NaN, with the same result).
+  if constexpr (CAUSAL) {
+    bool nonfinite = false;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) nonfinite |= !__builtin_isfinite(oacc[mb][r]);
+    if (__ballot(nonfinite) != 0)
+      exact_rows<D, CAUSAL, BLOCK>(
+          qg + b * p.q_sb + hq * p.q_sh, kg, vg, (__bf16*)p.o + b * p.o_sb + hq * p.o_sh,
+          p.lse != nullptr ? p.lse + ((int64_t)b * p.Hq + hq) * p.Nq : nullptr, p.q_ss, p.k_ss,
+          p.v_ss, p.o_ss, p.Nq, p.Nk, p.causal_off, p.scale_log2, p.block_mask, p.block_q,
+          p.block_k, p.nkb, q0, nrows);
   }
 }
 

@@ -128,10 +128,11 @@ size_t attn_fwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, i
  * stream   hipStream_t
  * A query row with no visible key yields O = 0 and LSE = -inf. Finite values
  * at positions a mask excludes never change a bit of the result, in every
- * softmax mode. Non-finite ones are never read under a BLOCK mask (dead
- * blocks) or past Nk; with bf16 inputs a NaN or Inf in V at a key the causal
- * rule hides from some rows of a 32-row group that sees other keys of the
- * same 64-key tile reaches those rows as 0 * NaN in the P V product. */
+ * softmax mode. Inf and NaN at excluded positions never reach a row that
+ * cannot see them either; at visible positions they propagate (IEEE). (Under
+ * the causal rule such a value can reach a hidden row's accumulator through
+ * a zero weight; a wave whose accumulators turn non-finite recomputes its
+ * rows pair by pair, which only inputs with such values pay for.) */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
              int mask_kind, const uint8_t* block_mask, int block_q, int block_k,
@@ -216,7 +217,9 @@ size_t attn_decode_multi_workspace_bytes(int B, int n_new, int Hq, int Hkv, int 
  * n_new    >= 1 with n_new * (Hq / Hkv) <= 16
  * other arguments as in attn_decode; workspace at least
  * attn_decode_multi_workspace_bytes(...) bytes. A row that sees no cached row
- * (seqlens[b] - n_new + t < 0) yields O = 0 and LSE = -inf. */
+ * (seqlens[b] - n_new + t < 0) yields O = 0 and LSE = -inf. An Inf or NaN in
+ * a later new token's own row never reaches an earlier token (a range whose
+ * accumulators turn non-finite is recomputed pair by pair). */
 int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* seqlens, void* o, float* lse, int dtype, int B, int n_new,
                       int Hq, int Hkv, int max_len, int d, float scale, int kv_splits,

@@ -75,6 +75,20 @@ def check(o_gpu, O_ref, lse_gpu=None, LSE_ref=None, dtype="bf16", where="", peak
     return mx
 
 
+def check_nonfinite(o_gpu, O_ref, lse_gpu, LSE_ref, where=""):
+    """Inputs with Inf/NaN values: non-finite outputs exactly where the oracle
+    has them (the rows that see a key with such a value, in that value's
+    columns), the rest within the band."""
+    o = to64(o_gpu)
+    bad_o, bad_ref = ~np.isfinite(o), ~np.isfinite(O_ref)
+    assert np.array_equal(bad_o, bad_ref), (
+        f"{where}: {int((bad_o & ~bad_ref).sum())} non-finite outputs the oracle has finite, "
+        f"{int((bad_ref & ~bad_o).sum())} the other way")
+    assert bad_ref.any(), f"{where}: the non-finite value must reach some row"
+    return check(np.where(bad_o, 0.0, o), np.where(bad_ref, 0.0, O_ref), lse_gpu, LSE_ref,
+                 where=where)
+
+
 GRAD_TOL = dict(rel_fro=1e-2, rel_max=2e-2)
 GRAD_ZERO_ABS = 1e-4
 

@@ -10,7 +10,7 @@ import oracle
 from exact_io_aware_attn_amd import attn_decode, attn_decode_multi, attn_decode_paged
 from exact_io_aware_attn_amd.inputs import WORKLOADS, decode_inputs, decode_multi_inputs
 
-from parity import check, to64
+from parity import check, check_nonfinite, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -204,6 +204,30 @@ def test_full_gqa_decode_b64_4tok_sampled():
         O, L = _multi_ref(ins["q"][b:b + 1].cpu(), ins["k_cache"][b:b + 1].cpu(),
                           ins["v_cache"][b:b + 1].cpu(), sl[b:b + 1].numpy(), w.scale)
         check(o[b:b + 1], O, lse[b:b + 1], L, where=f"gqa-decode-b64-4tok b={b}")
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("d,nt,kv_splits", [(64, 2, 0), (128, 4, 0), (128, 4, 7), (64, 3, 1)])
+def test_decode_multi_nonfinite_own_rows(d, nt, kv_splits, paged, bad):
+    """Inf or NaN in V at a new token's own cache row: the earlier new tokens,
+    which cannot see that row, get the same result as with finite values
+    there; the token itself and the later ones propagate it in its columns."""
+    seqlens, q, kc, vc = decode_multi_inputs(5, nt, 8, 2, 512, d, seed=nt + d + 3, len_lo=nt)
+    for b in range(5):
+        n = int(seqlens[b])
+        vc[b, n - 1, :, 0:4] = bad          # the last new token's row
+        vc[b, n - nt + 1, :, d - 8:] = bad  # the second new token's row
+    if paged:
+        kp, vp, table = _to_pages(kc, vc, 64, seed=d + nt)
+        o, lse = attn_decode_paged(q.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV),
+                                   seqlens.to(DEV), kv_splits=kv_splits)
+    else:
+        o, lse = attn_decode_multi(q.to(DEV), kc.to(DEV), vc.to(DEV), seqlens.to(DEV),
+                                   kv_splits=kv_splits)
+    torch.cuda.synchronize()
+    O, L = _multi_ref(q, kc, vc, seqlens.numpy(), 1 / math.sqrt(d))
+    check_nonfinite(o, O, lse, L, where=f"multi nonfinite d={d} nt={nt} paged={paged} {bad}")
 
 
 # ------------------------------------------------------------------ paged cache

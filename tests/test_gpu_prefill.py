@@ -14,7 +14,7 @@ import oracle
 from exact_io_aware_attn_amd import attn_fwd, attn_fwd_workspace_bytes, fixed_max_decisions
 from exact_io_aware_attn_amd.inputs import WORKLOADS, frame_block_mask, prefill_inputs
 
-from parity import check, sample_rows, to64
+from parity import check, check_nonfinite, sample_rows, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -368,6 +368,46 @@ def _workspace(B, Hq, Hkv, Nq, Nk, d, mode, mask_kind=1, bq=0, bk=0):
     from exact_io_aware_attn_amd.binding import SOFTMAX_MODES
     n = attn_fwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, mask_kind, bq, bk, SOFTMAX_MODES[mode])
     return torch.zeros(max(n, 1), dtype=torch.uint8, device=DEV)
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+@pytest.mark.parametrize("mode", ["online", "fixed_max", "fixed_max_centered"])
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d", [
+    (1, 4, 2, 300, 300, 128),     # 4-wave workgroups
+    (32, 16, 4, 300, 300, 128),   # 8-wave workgroups
+    (1, 4, 4, 520, 520, 64),      # keys split between two waves
+    (2, 4, 2, 200, 333, 64),      # Nq != Nk, ragged key tail
+])
+def test_nonfinite_v_at_causal_masked_keys(B, Hq, Hkv, Nq, Nk, d, mode, bad):
+    """Inf or NaN in V at keys inside diagonal tiles (some rows of a wave see
+    them, some do not): a row that cannot see such a key gets the same
+    result as with finite values there, a row that sees it propagates it in
+    that value's columns, as the oracle (which sums over visible keys only)."""
+    q, k, v = prefill_inputs(B, Hq, Hkv, Nq, Nk, d, torch.bfloat16, seed=Nk + d + B)
+    for t, cols in ((Nk // 2 + 5, slice(0, 8)), (Nk - 40, slice(d - 4, d))):
+        v[:, t, :, cols] = bad
+    ws = _workspace(B, Hq, Hkv, Nq, Nk, d, mode, 1)
+    o, lse = attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, softmax=mode, workspace=ws)
+    torch.cuda.synchronize()
+    O, L = _ref(q, k, v, 1 / math.sqrt(d), causal=True)
+    check_nonfinite(o, O, lse, L, f"{mode} {bad} B={B} H={Hq}/{Hkv} {Nq}x{Nk} d={d}")
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_nonfinite_v_causal_block_mask(bad):
+    """The same with a random block mask on top of the causal rule."""
+    rng = np.random.default_rng(11)
+    bq, bk = 48, 32
+    Nq, Nk = 12 * bq, 18 * bk
+    bm = (rng.random((Nq // bq, Nk // bk)) < 0.6).astype(np.uint8)
+    bm[:, 0] = 1
+    q, k, v = prefill_inputs(1, 4, 2, Nq, Nk, 128, torch.bfloat16, seed=12)
+    for t in (5 * bk + 7, 11 * bk + 20, Nk - 3):
+        v[:, t, :, 0:16] = bad
+    o, lse = attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, block_mask=bm, block=(bq, bk))
+    torch.cuda.synchronize()
+    O, L = _ref(q, k, v, 1 / math.sqrt(128), causal=True, block_mask=bm, block_q=bq, block_k=bk)
+    check_nonfinite(o, O, lse, L, f"block+causal {bad}")
 
 
 @pytest.mark.parametrize("frames,flen,blk,heads,g", [
