@@ -14,9 +14,10 @@ Printed (one JSON line):
              (4 d per attended query-key pair) over the prefill part of the steps
   decode     KV-read GB/s of the decode part (sum of lengths x Hkv x d x 2 x 2 B)
   roofline   prefill kernel against the dense bf16 MFMA peak (and against that peak
-             scaled to the kernel's sustained engine clock)
-  clock      the main kernel's sustained engine clock, from a counter pass of the
-             same bench command (GRBM_GUI_ACTIVE per XCD over the kernel's time),
+             scaled to the bounds on the kernel's sustained engine clock)
+  clock      bounds on the main kernel's sustained engine clock, from a counter
+             pass of the same bench command over the kernel's time: low from
+             SQ_BUSY_CYCLES per shader engine, high from GRBM_GUI_ACTIVE per XCD;
              stored in profiles/clock.json with a hash of the kernel sources
   roofline_decode  decode against the HBM peak
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample
@@ -97,11 +98,13 @@ def stored_clock(workload):
         return None
     if not _sources_match(rec):
         return None
-    return {"mhz": rec["mhz"], "kernel": rec["kernel"],
-            "source": "stored, not measured in this run: GRBM_GUI_ACTIVE / 8 XCDs over the "
-                      "kernel's duration in a rocprofv3 counter pass of the same bench command "
-                      "(profiles/clock.json); null whenever the kernel sources no longer match "
-                      "the hash stored with it"}
+    return {"mhz_low": rec["mhz_low"], "mhz_high": rec["mhz_high"], "kernel": rec["kernel"],
+            "source": "stored, not measured in this run: a rocprofv3 counter pass of the same "
+                      "bench command over the kernel's duration; low = SQ_BUSY_CYCLES / 32 "
+                      "shader engines (an engine out of work stops counting), high = "
+                      "GRBM_GUI_ACTIVE / 8 XCDs (includes the counter window); null whenever "
+                      "the kernel sources no longer match the hash stored with it "
+                      "(profiles/clock.json)"}
 
 
 def parse():
@@ -368,10 +371,12 @@ def main():
     clk = stored_clock(main_p.name)
     out["clock"] = clk
     if clk is not None and roof["bound"] == "mfma":
-        # the same peak at the engine clock the kernel held (the 2516.6 TFLOP/s
-        # figure assumes 2.4 GHz)
-        roof["peak_at_sustained_clock"] = roof["peak"] * clk["mhz"] / 2400.0
-        roof["frac_at_sustained_clock"] = roof["achieved"] / roof["peak_at_sustained_clock"]
+        # the same peak at the bounds on the engine clock the kernel held (the
+        # 2516.6 TFLOP/s figure assumes 2.4 GHz); the higher clock gives the
+        # lower fraction
+        pk = [roof["peak"] * clk[m] / 2400.0 for m in ("mhz_low", "mhz_high")]
+        roof["peak_at_sustained_clock"] = pk
+        roof["frac_at_sustained_clock"] = [roof["achieved"] / pk[1], roof["achieved"] / pk[0]]
     out["roofline"] = roof
     if len(parts) > 1 and parts[1].kind == "decode":
         d = parts[1]
