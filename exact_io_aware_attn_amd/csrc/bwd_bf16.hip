@@ -10,14 +10,17 @@
 // where D_i = dO_i . O_i equals sum_j P_ij dP_ij (the row term of the softmax
 // Jacobian). Three kernels, no atomics (outputs are bitwise repeatable):
 //  * bwd_prep_kernel: D_i and LSE_i * log2(e) per row into the workspace.
-//  * bwd_dkdv_kernel: keys stationary (32 per wave, 128 per workgroup), K and
+//  * dK and dV: keys stationary (32 per key block, 128 per workgroup), K and
 //    V in registers; Q and dO tiles of 64 rows stream through LDS for every
-//    query head of the group, so dK and dV sum the group in registers.
+//    query head of the group, so dK and dV sum the group in registers. At
+//    d = 64 one wave holds a key block (bwd_dkdv_kernel); at d = 128 two
+//    waves share it, one holding K and dV, the other V and dK
+//    (bwd_dkdv_split_kernel).
 //  * bwd_dq_kernel: queries stationary (32 per wave), Q and dO in registers;
 //    K and V tiles of 64 keys stream through LDS.
-// Both main kernels stage tiles HBM -> LDS with the LDS-DMA loads the forward
-// kernel uses (rows past the end read as zeros), double-buffered with one
-// barrier per tile, and skip tiles the causal rule hides entirely.
+// The main kernels stage tiles HBM -> LDS with the LDS-DMA loads the forward
+// kernel uses (rows past the end read as zeros), with one barrier per tile,
+// and skip tiles the causal rule hides entirely.
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -29,13 +32,38 @@ namespace {
 constexpr int BT = 64;  // rows of a streamed tile (queries or keys)
 constexpr int NW = 4;   // waves per workgroup, 32 stationary rows each
 
+// LDS swizzle (row r, logical 16-byte chunk ch -> slot) for the tiles this
+// pass reads both as rows and through the transpose load (Q and dO in dK/dV,
+// K in dQ). A row read serves 16 lanes with 16 consecutive rows of one chunk;
+// a transpose read serves 32 lanes with 4 consecutive rows (aligned to 4) of 4
+// consecutive chunks. The row term is a permutation over each aligned run of
+// 16 rows (d = 128; over each parity class of them at d = 64, where two rows
+// share the 256 bytes of the banks) whose high bits differ within every
+// aligned run of 4 rows, so neither read meets a bank twice. An involution.
+template <int D>
+__device__ __forceinline__ int bswz(int r, int ch) {
+  if constexpr (D == 128) return ch ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  else return ch ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// The layout of a streamed tile: kswz (read as rows only), vswz (read both
+// ways; the dQ kernel's K tile, where the extra address registers of bswz
+// would spill) or bswz.
+enum { SW_K = 0, SW_V = 1, SW_B = 2 };
+template <int D, int SW>
+__device__ __forceinline__ int swz(int r, int ch) {
+  if constexpr (SW == SW_K) return kswz<D>(r, ch);
+  else if constexpr (SW == SW_V) return vswz<D>(r, ch);
+  else return bswz<D>(r, ch);
+}
+
 // A-operand fragment of a [BT][D] LDS tile read as rows: lane (i, h) gets row
-// 32*blk + i, elements 16*ks + 8*h .. +8 (TR: the tile uses vswz, else kswz).
-template <int D, bool TR>
+// 32*blk + i, elements 16*ks + 8*h .. +8.
+template <int D, int SW>
 __device__ __forceinline__ bf16x8 row_frag(const __bf16* t, int blk, int ks, int qc, int h) {
   const int row = 32 * blk + qc;
   const int ch = 2 * ks + h;
-  const int slot = TR ? vswz<D>(row, ch) : kswz<D>(row, ch);
+  const int slot = swz<D, SW>(row, ch);
   return *(const bf16x8*)(t + row * D + slot * 8);
 }
 
@@ -43,13 +71,13 @@ __device__ __forceinline__ bf16x8 row_frag(const __bf16* t, int blk, int ks, int
 // 32-column block mb: lane (i, h') gets columns 32*mb + i of rows
 // 16u + 8*(e/4) + 4h' + e%4, e = 0..7 -- the row order in which the 32x32
 // accumulator holds them, so the accumulator serves as the B operand as is.
-template <int D>
+template <int D, int SW>
 __device__ __forceinline__ bf16x8 tr_frag(const __bf16* t, int u, int mb, int tr_row, int tr_ch,
                                           int tr_half) {
   const int ch = 4 * mb + tr_ch;
   const int r0 = 16 * u + tr_row, r1 = 16 * u + 8 + tr_row;
-  const s16x4 lo = lds_tr16(t + r0 * D + vswz<D>(r0, ch) * 8 + tr_half);
-  const s16x4 hi = lds_tr16(t + r1 * D + vswz<D>(r1, ch) * 8 + tr_half);
+  const s16x4 lo = lds_tr16(t + r0 * D + swz<D, SW>(r0, ch) * 8 + tr_half);
+  const s16x4 hi = lds_tr16(t + r1 * D + swz<D, SW>(r1, ch) * 8 + tr_half);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -138,15 +166,20 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const BwdParams p) {
 // holding key c for the 16 query rows 8*(r/4) + 4h + r%4 of a 32-row block;
 // P and dS in that layout are the B operands of dV^T += dO^T P and
 // dK^T += Q^T dS, whose A operands are transposed reads of the dO and Q tiles.
-// d = 128 holds K, V and both accumulators (192 registers) plus the tile's
-// S and dP: one wave per SIMD, so nothing spills.
+// Used at d = 64, where K, V and both accumulators (96 registers) leave room
+// for two waves per SIMD; d = 128 splits each key block over two waves
+// (bwd_dkdv_split_kernel below).
 template <int D, bool CAUSAL, bool BLOCK>
-__global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(const BwdParams p) {
+__global__ void __launch_bounds__(64 * NW, 2) bwd_dkdv_kernel(const BwdParams p) {
+  static_assert(D == 64, "d = 128 runs bwd_dkdv_split_kernel");
   constexpr int CH = D / 8;
   constexpr int KSTEPS = D / 16;
   constexpr int MB = D / 32;
   constexpr int RPI = 1024 / (D * 2);  // tile rows per 1 KiB load instruction
   constexpr int NIW = BT / RPI / NW;   // load instructions per wave per tile and tensor
+  // Q and dO layout: vswz; bswz's extra address arithmetic measured slower
+  // here than the row reads' bank conflicts
+  constexpr int SWT = SW_V;
 
   __shared__ __attribute__((aligned(16))) __bf16 sQ[2][BT * D];
   __shared__ __attribute__((aligned(16))) __bf16 sG[2][BT * D];    // dO
@@ -208,15 +241,15 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
   const int n_steps = G * n_qt;  // step s: query head hkv*G + s / n_qt, tile s % n_qt
 
   // ---- staging: instruction j of this wave fills tile rows
-  // (wave*NIW + j)*RPI + lane/CH, LDS slot lane%CH holding chunk vswz(r, slot)
+  // (wave*NIW + j)*RPI + lane/CH, LDS slot lane%CH holding chunk swz(r, slot)
   const int dma_row0 = wave * NIW * RPI + lane / CH;
   const int dma_slot = lane % CH;
   uint32_t qo[NIW], go[NIW];
 #pragma unroll
   for (int j = 0; j < NIW; ++j) {
     const int r = dma_row0 + j * RPI;
-    qo[j] = (uint32_t)(r * p.q_ss + vswz<D>(r, dma_slot) * 8) * 2u;
-    go[j] = (uint32_t)(r * p.do_ss + vswz<D>(r, dma_slot) * 8) * 2u;
+    qo[j] = (uint32_t)(r * p.q_ss + swz<D, SWT>(r, dma_slot) * 8) * 2u;
+    go[j] = (uint32_t)(r * p.do_ss + swz<D, SWT>(r, dma_slot) * 8) * 2u;
   }
   const int64_t nstat = (int64_t)p.B * p.Hq * p.npad;
   const DmaRsrc rst = dma_rsrc(p.stats, (uint32_t)(2 * nstat * 4));
@@ -261,8 +294,8 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
     dp = f32x16{};
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
-      s = mfma32(row_frag<D, true>(sq, qb, t, qc, h), kf[t], s);
-      dp = mfma32(row_frag<D, true>(sg, qb, t, qc, h), vf[t], dp);
+      s = mfma32(row_frag<D, SWT>(sq, qb, t, qc, h), kf[t], s);
+      dp = mfma32(row_frag<D, SWT>(sg, qb, t, qc, h), vf[t], dp);
     }
   };
   // P = exp2(c s - lse2) into s and dS = P (dP - D) into dp, rows 8j + 4h + i
@@ -317,121 +350,9 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
                              dp[o8 + 5], dp[o8 + 6], dp[o8 + 7]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        dvacc[mb] = mfma32(tr_frag<D>(sg, u, mb, tr_row, tr_ch, tr_half), pf, dvacc[mb]);
-        dkacc[mb] = mfma32(tr_frag<D>(sq, u, mb, tr_row, tr_ch, tr_half), df, dkacc[mb]);
+        dvacc[mb] = mfma32(tr_frag<D, SWT>(sg, u, mb, tr_row, tr_ch, tr_half), pf, dvacc[mb]);
+        dkacc[mb] = mfma32(tr_frag<D, SWT>(sq, u, mb, tr_row, tr_ch, tr_half), df, dkacc[mb]);
       }
-    }
-  };
-
-  // Both 32-query blocks of a tile fully visible, d = 128 (one wave per SIMD,
-  // so the wave's own issue order decides what overlaps; at d = 64 two waves
-  // share a SIMD and the fixed order measured slower): four straight-line
-  // stages with a fixed order (sched_barrier between steps), each MFMA step
-  // carrying one element of softmax work and the LDS reads of the operands
-  // two products ahead --
-  //   A. block 0's S and dP products
-  //   B. block 1's S and dP products, block 0's softmax
-  //   C. block 0's dV and dK products, block 1's softmax
-  //   D. block 1's dV and dK products
-  constexpr int NPB = 2 * KSTEPS;  // products per stage (16 at d = 128, 8 at d = 64)
-  constexpr int LEAD = 2;
-  constexpr int SPP = 16 / NPB;    // softmax steps per product (17 steps: the last after)
-  auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
-  auto fast = [&](const __bf16* sq, const __bf16* sg, const float* ss)
-      __attribute__((always_inline)) {
-    // operand i of a score stage: S (even, Q rows) or dP (odd, dO rows)
-    auto sc_op = [&](int qb, int i) __attribute__((always_inline)) {
-      return row_frag<D, true>((i & 1) ? sg : sq, qb, i >> 1, qc, h);
-    };
-    // operand i of a gradient stage: dV (even, dO^T) or dK (odd, Q^T), step
-    // u = 2 qb + i / (2 MB), column block (i % (2 MB)) / 2
-    auto gr_op = [&](int qb, int i) __attribute__((always_inline)) {
-      return tr_frag<D>((i & 1) ? sq : sg, 2 * qb + i / (2 * MB), (i % (2 * MB)) >> 1, tr_row,
-                        tr_ch, tr_half);
-    };
-    f32x4 st4[2][2][4];  // [block][lse2, dsum][j]
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        st4[qb][0][j] = *(const f32x4*)(ss + 32 * qb + 8 * j + 4 * h);
-        st4[qb][1][j] = *(const f32x4*)(ss + BT + 32 * qb + 8 * j + 4 * h);
-      }
-    f32x16 sb[2], db[2];
-    // softmax step j of block qb: P of element j, dS of element j - 1
-    auto sm_step = [&](int qb, int j) __attribute__((always_inline)) {
-      if (j < 16) sb[qb][j] = ex2(__builtin_fmaf(sb[qb][j], c, -st4[qb][0][j >> 2][j & 3]));
-      if (j >= 1) {
-        const int e = j - 1;
-        db[qb][e] = sb[qb][e] * (db[qb][e] - st4[qb][1][e >> 2][e & 3]);
-      }
-    };
-    bf16x8 op[NPB];
-#pragma unroll
-    for (int i = 0; i < LEAD; ++i) op[i] = sc_op(0, i);
-    sb[0] = f32x16{};
-    db[0] = f32x16{};
-    sb[1] = f32x16{};
-    db[1] = f32x16{};
-    fence();
-    // A
-#pragma unroll
-    for (int i = 0; i < NPB; ++i) {
-      if (i & 1) db[0] = mfma32(op[i], vf[i >> 1], db[0]);
-      else sb[0] = mfma32(op[i], kf[i >> 1], sb[0]);
-      if (i + LEAD < NPB) op[i + LEAD] = sc_op(0, i + LEAD);
-      else op[i + LEAD - NPB] = sc_op(1, i + LEAD - NPB);
-      fence();
-    }
-    // B
-#pragma unroll
-    for (int i = 0; i < NPB; ++i) {
-      if (i & 1) db[1] = mfma32(op[i], vf[i >> 1], db[1]);
-      else sb[1] = mfma32(op[i], kf[i >> 1], sb[1]);
-      if (i + LEAD < NPB) op[i + LEAD] = sc_op(1, i + LEAD);
-      else op[i + LEAD - NPB] = gr_op(0, i + LEAD - NPB);
-#pragma unroll
-      for (int k = 0; k < SPP; ++k) sm_step(0, i * SPP + k);
-      fence();
-    }
-#pragma unroll
-    for (int j = NPB * SPP; j <= 16; ++j) sm_step(0, j);
-    bf16x8 pf = cvt8(sb[0][0], sb[0][1], sb[0][2], sb[0][3], sb[0][4], sb[0][5], sb[0][6], sb[0][7]);
-    bf16x8 df = cvt8(db[0][0], db[0][1], db[0][2], db[0][3], db[0][4], db[0][5], db[0][6], db[0][7]);
-    fence();
-    // C
-#pragma unroll
-    for (int i = 0; i < NPB; ++i) {
-      if (i == 2 * MB) {
-        pf = cvt8(sb[0][8], sb[0][9], sb[0][10], sb[0][11], sb[0][12], sb[0][13], sb[0][14], sb[0][15]);
-        df = cvt8(db[0][8], db[0][9], db[0][10], db[0][11], db[0][12], db[0][13], db[0][14], db[0][15]);
-      }
-      const int mb = (i % (2 * MB)) >> 1;
-      if (i & 1) dkacc[mb] = mfma32(op[i], df, dkacc[mb]);
-      else dvacc[mb] = mfma32(op[i], pf, dvacc[mb]);
-      if (i + LEAD < NPB) op[i + LEAD] = gr_op(0, i + LEAD);
-      else op[i + LEAD - NPB] = gr_op(1, i + LEAD - NPB);
-#pragma unroll
-      for (int k = 0; k < SPP; ++k) sm_step(1, i * SPP + k);
-      fence();
-    }
-#pragma unroll
-    for (int j = NPB * SPP; j <= 16; ++j) sm_step(1, j);
-    pf = cvt8(sb[1][0], sb[1][1], sb[1][2], sb[1][3], sb[1][4], sb[1][5], sb[1][6], sb[1][7]);
-    df = cvt8(db[1][0], db[1][1], db[1][2], db[1][3], db[1][4], db[1][5], db[1][6], db[1][7]);
-    fence();
-    // D
-#pragma unroll
-    for (int i = 0; i < NPB; ++i) {
-      if (i == 2 * MB) {
-        pf = cvt8(sb[1][8], sb[1][9], sb[1][10], sb[1][11], sb[1][12], sb[1][13], sb[1][14], sb[1][15]);
-        df = cvt8(db[1][8], db[1][9], db[1][10], db[1][11], db[1][12], db[1][13], db[1][14], db[1][15]);
-      }
-      const int mb = (i % (2 * MB)) >> 1;
-      if (i & 1) dkacc[mb] = mfma32(op[i], df, dkacc[mb]);
-      else dvacc[mb] = mfma32(op[i], pf, dvacc[mb]);
-      if (i + LEAD < NPB) op[i + LEAD] = gr_op(1, i + LEAD);
-      fence();
     }
   };
 
@@ -456,10 +377,6 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
         const int bs = block_state(p, qs, min(qs + 31, p.Nq - 1), k0w, min(k0w + 31, p.Nk - 1));
         state[qb] = bs == 0 ? 0 : (bs == 2 ? 2 : state[qb]);
       }
-    }
-    if (D == 128 && state[0] == 1 && state[1] == 1) {
-      fast(sq, sg, ss);
-      return;
     }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -498,6 +415,432 @@ __global__ void __launch_bounds__(64 * NW, D == 128 ? 1 : 2) bwd_dkdv_kernel(con
                  a[4 * jj + 3] * p.scale);
         *(bf16x4*)(dvp + 32 * mb + 8 * jj + 4 * h) =
             cvt4(v[4 * jj], v[4 * jj + 1], v[4 * jj + 2], v[4 * jj + 3]);
+      }
+  }
+}
+
+// ---- dK and dV at d = 128 with each 32-key block's work split over two
+// waves, so that each holds half the stationary registers and two waves share
+// a SIMD. Workgroup: 128 keys of one (batch, KV head), 8 waves; waves w and
+// w + 4 cover keys 32w .. 32w+31 (lane (c, h): key c, elements 16t + 8h):
+//  * wave w (the P wave) holds K and accumulates dV^T: S = Q K^T, P =
+//    exp2(c S - lse2) with the masks, P to LDS as bf16, dV^T += dO^T P;
+//  * wave w + 4 (the dS wave) holds V and accumulates dK^T: dP = dO V^T, P
+//    from LDS, dS = P (dP - D), dK^T += Q^T dS.
+// The dS wave runs one tile behind the P wave, so one barrier per tile
+// publishes both a tile's P and the next tile's Q and dO: three Q/dO buffers
+// (the P wave's tile, the dS wave's tile, the one loading) and two P buffers.
+// Fragment layouts and the order of products into each accumulator are the
+// d = 64 kernel's; dS is formed from the bf16 P that dV also consumes. Q and
+// dO sit in LDS as bswz (under vswz the row reads meet each bank four times).
+constexpr int NWS = 8;
+
+template <bool CAUSAL, bool BLOCK>
+__global__ void __launch_bounds__(64 * NWS, 2) bwd_dkdv_split_kernel(const BwdParams p) {
+  constexpr int D = 128;
+  constexpr int CH = D / 8;
+  constexpr int KSTEPS = D / 16;
+  constexpr int MB = D / 32;
+  constexpr int RPI = 1024 / (D * 2);
+  constexpr int NIW = BT / RPI / NWS;  // load instructions per wave per tile and tensor
+
+  __shared__ __attribute__((aligned(16))) __bf16 sQ[3][BT * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sG[3][BT * D];   // dO
+  __shared__ __attribute__((aligned(16))) float sSt[3][2 * BT];  // lse2 then dsum
+  __shared__ bf16x8 sP[2][NW][2][2][64];  // [buffer][key block][query block][half][lane]
+  __shared__ short sTile[BLOCK ? kMaxBwdTiles : 1];
+  __shared__ int sNT;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kw = wave & (NW - 1);  // key block of the wave
+  const bool pw = wave < NW;       // P wave (else dS wave)
+  const int qc = lane & 31;
+  const int h = lane >> 5;
+
+  const int nbh = p.B * p.Hkv;
+  const int bh = blockIdx.x % nbh;
+  const int kt = blockIdx.x / nbh;
+  const int b = bh / p.Hkv;
+  const int hkv = bh % p.Hkv;
+  const int G = p.Hq / p.Hkv;
+  const int k0w = kt * 128 + 32 * kw;
+  const int key = k0w + qc;
+  const bool key_ok = key < p.Nk;
+
+  // stationary fragments: K (P wave) or V (dS wave)
+  bf16x8 sf[KSTEPS];
+  {
+    const __bf16* sp = pw ? (const __bf16*)p.k + b * p.k_sb + (int64_t)key * p.k_ss + hkv * p.k_sh
+                          : (const __bf16*)p.v + b * p.v_sb + (int64_t)key * p.v_ss + hkv * p.v_sh;
+    const bf16x8 z = {};
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) sf[t] = key_ok ? *(const bf16x8*)(sp + 8 * h + 16 * t) : z;
+  }
+
+  int qb0 = 0;
+  if constexpr (CAUSAL) qb0 = max(0, kt * 128 - p.causal_off) / BT * BT;
+  int n_qt = p.Nq > qb0 ? (p.Nq - qb0 + BT - 1) / BT : 0;
+  if constexpr (BLOCK) {
+    if (wave == 0) {
+      const int kb0 = kt * 128 / p.block_k, kb1 = (min(kt * 128 + 128, p.Nk) - 1) / p.block_k;
+      const int n = live_tiles<false>(
+          p, qb0 / BT, (p.Nq + BT - 1) / BT, kb0, kb1,
+          [&](int t, int& a, int& b) {
+            a = t * BT / p.block_q;
+            b = (min(t * BT + BT, p.Nq) - 1) / p.block_q;
+          },
+          sTile, lane);
+      if (lane == 0) sNT = n;
+    }
+    __syncthreads();
+    n_qt = sNT;
+  }
+  auto tile_row = [&](int i) { return BLOCK ? (int)sTile[i] * BT : qb0 + i * BT; };
+  const int n_steps = G * n_qt;
+
+  const int dma_row0 = wave * NIW * RPI + lane / CH;
+  const int dma_slot = lane % CH;
+  uint32_t qo[NIW], go[NIW];
+#pragma unroll
+  for (int j = 0; j < NIW; ++j) {
+    const int r = dma_row0 + j * RPI;
+    qo[j] = (uint32_t)(r * p.q_ss + bswz<D>(r, dma_slot) * 8) * 2u;
+    go[j] = (uint32_t)(r * p.do_ss + bswz<D>(r, dma_slot) * 8) * 2u;
+  }
+  const int64_t nstat = (int64_t)p.B * p.Hq * p.npad;
+  const DmaRsrc rst = dma_rsrc(p.stats, (uint32_t)(2 * nstat * 4));
+  auto issue = [&](int st, int buf) {
+    const int g = st / n_qt;
+    const int r0 = tile_row(st - g * n_qt);
+    const int hq = hkv * G + g;
+    const int nvalid = min(BT, p.Nq - r0);
+    const __bf16* qb = (const __bf16*)p.q + b * p.q_sb + (int64_t)r0 * p.q_ss + hq * p.q_sh;
+    const __bf16* gb = (const __bf16*)p.dout + b * p.do_sb + (int64_t)r0 * p.do_ss + hq * p.do_sh;
+    const DmaRsrc rq = dma_rsrc(qb, span<D>(nvalid, p.q_ss));
+    const DmaRsrc rg = dma_rsrc(gb, span<D>(nvalid, p.do_ss));
+#pragma unroll
+    for (int j = 0; j < NIW; ++j) {
+      const int lds_row = (wave * NIW + j) * RPI;
+      buf_load_lds16(rq, sQ[buf] + lds_row * D, qo[j]);
+      buf_load_lds16(rg, sG[buf] + lds_row * D, go[j]);
+    }
+    if (wave == 0 && lane < 32) {
+      const int64_t srow = ((int64_t)b * p.Hq + hq) * p.npad + r0;
+      const uint32_t off = (uint32_t)((srow + (lane >= 16 ? nstat : 0)) * 4 + 16 * (lane & 15));
+      buf_load_lds16(rst, sSt[buf], off);
+    }
+  };
+
+  f32x16 acc[MB];  // dV^T (P wave) or dK^T (dS wave)
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+  const float c = p.scale_log2;
+  const int tr_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_ch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_half = 4 * (lane & 1);
+  const int key_blk = (BLOCK && key_ok) ? key / p.block_k : 0;
+
+  // per 32-query block of the tile at row r0: 0 no pair visible, 1 all
+  // visible, 2 apply the masks element by element (the same for both waves)
+  auto states = [&](int r0, int* state) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qs = r0 + 32 * qb;
+      state[qb] = 1;
+      if (qs >= p.Nq || k0w >= p.Nk) state[qb] = 0;
+      else if (CAUSAL) {
+        if (qs + 31 + p.causal_off < k0w) state[qb] = 0;
+        else if (qs + p.causal_off < k0w + 31) state[qb] = 2;
+      }
+      if (BLOCK && state[qb] != 0) {
+        const int bs = block_state(p, qs, min(qs + 31, p.Nq - 1), k0w, min(k0w + 31, p.Nk - 1));
+        state[qb] = bs == 0 ? 0 : (bs == 2 ? 2 : state[qb]);
+      }
+    }
+  };
+
+  // P wave, a tile with a masked or empty block: block by block
+  auto p_general = [&](int r0, const int* state, const __bf16* sq, const __bf16* sg, const float* ss,
+                       bf16x8* pdst) {
+    f32x16 s[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      if (state[qb] == 0) continue;
+      s[qb] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t) s[qb] = mfma32(row_frag<D, SW_B>(sq, qb, t, qc, h), sf[t], s[qb]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      if (state[qb] == 0) continue;
+      const int qs = r0 + 32 * qb;
+      const bool masked = state[qb] == 2;
+      bool fl0 = false, fl1 = false, fl2 = false;
+      int qbb1 = 0, qbb2 = 0;
+      if (BLOCK && masked) {
+        const int qbk = qs / p.block_q, nqb = p.Nq / p.block_q;
+        qbb1 = (qbk + 1) * p.block_q;
+        qbb2 = (qbk + 2) * p.block_q;
+        const uint8_t* col = p.block_mask + key_blk;
+        if (key_ok) {
+          fl0 = col[(int64_t)qbk * p.nkb] != 0;
+          fl1 = qbk + 1 < nqb && col[(int64_t)(qbk + 1) * p.nkb] != 0;
+          fl2 = qbk + 2 < nqb && col[(int64_t)(qbk + 2) * p.nkb] != 0;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 l4 = *(const f32x4*)(ss + 32 * qb + 8 * j + 4 * h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * j + i;
+          float pr = ex2(__builtin_fmaf(s[qb][r], c, -l4[i]));
+          if ((CAUSAL || BLOCK) && masked) {
+            const int q = qs + 8 * j + 4 * h + i;
+            bool ok = true;
+            if (CAUSAL) ok = key <= q + p.causal_off;
+            if (BLOCK) ok = ok && q < p.Nq && (q >= qbb2 ? fl2 : q >= qbb1 ? fl1 : fl0);
+            pr = ok ? pr : 0.f;
+          }
+          s[qb][r] = pr;
+        }
+      }
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const int o8 = 8 * uu;
+        const bf16x8 pf = cvt8(s[qb][o8 + 0], s[qb][o8 + 1], s[qb][o8 + 2], s[qb][o8 + 3],
+                               s[qb][o8 + 4], s[qb][o8 + 5], s[qb][o8 + 6], s[qb][o8 + 7]);
+        pdst[(qb * 2 + uu) * 64 + lane] = pf;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb] = mfma32(tr_frag<D, SW_B>(sg, 2 * qb + uu, mb, tr_row, tr_ch, tr_half), pf, acc[mb]);
+      }
+    }
+  };
+
+  // dS wave, a tile with a masked or empty block: block by block
+  auto ds_general = [&](const int* state, const __bf16* sq, const __bf16* sg, const float* ss,
+                        const bf16x8* psrc) {
+    f32x16 dp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      if (state[qb] == 0) continue;
+      dp[qb] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t) dp[qb] = mfma32(row_frag<D, SW_B>(sg, qb, t, qc, h), sf[t], dp[qb]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      if (state[qb] == 0) continue;
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const bf16x8 pf = psrc[(qb * 2 + uu) * 64 + lane];
+        const f32x4 d0 = *(const f32x4*)(ss + BT + 32 * qb + 16 * uu + 4 * h);
+        const f32x4 d1 = *(const f32x4*)(ss + BT + 32 * qb + 16 * uu + 8 + 4 * h);
+        float ds[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float dsum = e < 4 ? d0[e] : d1[e - 4];
+          ds[e] = bf2f(pf[e]) * (dp[qb][8 * uu + e] - dsum);
+        }
+        const bf16x8 df = cvt8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb] = mfma32(tr_frag<D, SW_B>(sq, 2 * qb + uu, mb, tr_row, tr_ch, tr_half), df, acc[mb]);
+      }
+    }
+  };
+
+  // Both 32-query blocks fully visible: four straight-line stages in a fixed
+  // order (sched_barrier between steps), the LDS operands read two products
+  // ahead and the elementwise work of one block spread over the other's
+  // products. The products reach each accumulator in the block-by-block
+  // order, so results are bitwise those of the general path.
+  //   P wave:  S(b0) | S(b1), P(b0) | dV(b0), P(b1) | dV(b1)
+  //   dS wave: dP(b0) | dP(b1), dS(b0) | dK(b0), dS(b1) | dK(b1)
+  auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+  constexpr int LEAD = 2;
+  // sc: row operand t of block qb (S or dP); gr: transposed operand i of block
+  // qb (step u = 2 qb + i / MB, column block i % MB)
+  auto p_fast = [&](const __bf16* sq, const __bf16* sg, const float* ss, bf16x8* pdst)
+      __attribute__((always_inline)) {
+    auto sc = [&](int qb, int t) __attribute__((always_inline)) { return row_frag<D, SW_B>(sq, qb, t, qc, h); };
+    auto gr = [&](int qb, int i) __attribute__((always_inline)) {
+      return tr_frag<D, SW_B>(sg, 2 * qb + i / MB, i % MB, tr_row, tr_ch, tr_half);
+    };
+    f32x4 l4[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) l4[qb][j] = *(const f32x4*)(ss + 32 * qb + 8 * j + 4 * h);
+    f32x16 sb[2];
+    sb[0] = f32x16{};
+    sb[1] = f32x16{};
+    auto sm = [&](int qb, int j) __attribute__((always_inline)) {
+      sb[qb][j] = ex2(__builtin_fmaf(sb[qb][j], c, -l4[qb][j >> 2][j & 3]));
+    };
+    bf16x8 op[KSTEPS];
+#pragma unroll
+    for (int i = 0; i < LEAD; ++i) op[i] = sc(0, i);
+    fence();
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) {
+      sb[0] = mfma32(op[i], sf[i], sb[0]);
+      if (i + LEAD < KSTEPS) op[i + LEAD] = sc(0, i + LEAD);
+      else op[i + LEAD - KSTEPS] = sc(1, i + LEAD - KSTEPS);
+      fence();
+    }
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) {
+      sb[1] = mfma32(op[i], sf[i], sb[1]);
+      if (i + LEAD < KSTEPS) op[i + LEAD] = sc(1, i + LEAD);
+      else op[i + LEAD - KSTEPS] = gr(0, i + LEAD - KSTEPS);
+      sm(0, 2 * i);
+      sm(0, 2 * i + 1);
+      fence();
+    }
+    bf16x8 pf0 = cvt8(sb[0][0], sb[0][1], sb[0][2], sb[0][3], sb[0][4], sb[0][5], sb[0][6], sb[0][7]);
+    bf16x8 pf1 = cvt8(sb[0][8], sb[0][9], sb[0][10], sb[0][11], sb[0][12], sb[0][13], sb[0][14], sb[0][15]);
+    pdst[0 * 64 + lane] = pf0;
+    pdst[1 * 64 + lane] = pf1;
+    fence();
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) {
+      acc[i % MB] = mfma32(op[i], i < MB ? pf0 : pf1, acc[i % MB]);
+      if (i + LEAD < KSTEPS) op[i + LEAD] = gr(0, i + LEAD);
+      else op[i + LEAD - KSTEPS] = gr(1, i + LEAD - KSTEPS);
+      sm(1, 2 * i);
+      sm(1, 2 * i + 1);
+      fence();
+    }
+    pf0 = cvt8(sb[1][0], sb[1][1], sb[1][2], sb[1][3], sb[1][4], sb[1][5], sb[1][6], sb[1][7]);
+    pf1 = cvt8(sb[1][8], sb[1][9], sb[1][10], sb[1][11], sb[1][12], sb[1][13], sb[1][14], sb[1][15]);
+    pdst[2 * 64 + lane] = pf0;
+    pdst[3 * 64 + lane] = pf1;
+    fence();
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) {
+      acc[i % MB] = mfma32(op[i], i < MB ? pf0 : pf1, acc[i % MB]);
+      if (i + LEAD < KSTEPS) op[i + LEAD] = gr(1, i + LEAD);
+      fence();
+    }
+  };
+  auto ds_fast = [&](const __bf16* sq, const __bf16* sg, const float* ss, const bf16x8* psrc)
+      __attribute__((always_inline)) {
+    auto sc = [&](int qb, int t) __attribute__((always_inline)) { return row_frag<D, SW_B>(sg, qb, t, qc, h); };
+    auto gr = [&](int qb, int i) __attribute__((always_inline)) {
+      return tr_frag<D, SW_B>(sq, 2 * qb + i / MB, i % MB, tr_row, tr_ch, tr_half);
+    };
+    bf16x8 pv[2][2];
+    f32x4 d4[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) pv[qb][uu] = psrc[(qb * 2 + uu) * 64 + lane];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d4[qb][j] = *(const f32x4*)(ss + BT + 32 * qb + 8 * j + 4 * h);
+    }
+    f32x16 db[2];
+    db[0] = f32x16{};
+    db[1] = f32x16{};
+    auto dss = [&](int qb, int e) __attribute__((always_inline)) {
+      db[qb][e] = bf2f(pv[qb][e >> 3][e & 7]) * (db[qb][e] - d4[qb][e >> 2][e & 3]);
+    };
+    bf16x8 op[KSTEPS];
+#pragma unroll
+    for (int i = 0; i < LEAD; ++i) op[i] = sc(0, i);
+    fence();
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) {
+      db[0] = mfma32(op[i], sf[i], db[0]);
+      if (i + LEAD < KSTEPS) op[i + LEAD] = sc(0, i + LEAD);
+      else op[i + LEAD - KSTEPS] = sc(1, i + LEAD - KSTEPS);
+      fence();
+    }
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) {
+      db[1] = mfma32(op[i], sf[i], db[1]);
+      if (i + LEAD < KSTEPS) op[i + LEAD] = sc(1, i + LEAD);
+      else op[i + LEAD - KSTEPS] = gr(0, i + LEAD - KSTEPS);
+      dss(0, 2 * i);
+      dss(0, 2 * i + 1);
+      fence();
+    }
+    bf16x8 df0 = cvt8(db[0][0], db[0][1], db[0][2], db[0][3], db[0][4], db[0][5], db[0][6], db[0][7]);
+    bf16x8 df1 = cvt8(db[0][8], db[0][9], db[0][10], db[0][11], db[0][12], db[0][13], db[0][14], db[0][15]);
+    fence();
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) {
+      acc[i % MB] = mfma32(op[i], i < MB ? df0 : df1, acc[i % MB]);
+      if (i + LEAD < KSTEPS) op[i + LEAD] = gr(0, i + LEAD);
+      else op[i + LEAD - KSTEPS] = gr(1, i + LEAD - KSTEPS);
+      dss(1, 2 * i);
+      dss(1, 2 * i + 1);
+      fence();
+    }
+    df0 = cvt8(db[1][0], db[1][1], db[1][2], db[1][3], db[1][4], db[1][5], db[1][6], db[1][7]);
+    df1 = cvt8(db[1][8], db[1][9], db[1][10], db[1][11], db[1][12], db[1][13], db[1][14], db[1][15]);
+    fence();
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) {
+      acc[i % MB] = mfma32(op[i], i < MB ? df0 : df1, acc[i % MB]);
+      if (i + LEAD < KSTEPS) op[i + LEAD] = gr(1, i + LEAD);
+      fence();
+    }
+  };
+
+  auto tile_p = [&](int st, int buf, bf16x8* pdst) {
+    const int g = st / n_qt;
+    const int r0 = tile_row(st - g * n_qt);
+    int state[2];
+    states(r0, state);
+    if (state[0] == 1 && state[1] == 1) p_fast(sQ[buf], sG[buf], sSt[buf], pdst);
+    else p_general(r0, state, sQ[buf], sG[buf], sSt[buf], pdst);
+  };
+  auto tile_ds = [&](int st, int buf, const bf16x8* psrc) {
+    const int g = st / n_qt;
+    const int r0 = tile_row(st - g * n_qt);
+    int state[2];
+    states(r0, state);
+    if (state[0] == 1 && state[1] == 1) ds_fast(sQ[buf], sG[buf], sSt[buf], psrc);
+    else ds_general(state, sQ[buf], sG[buf], sSt[buf], psrc);
+  };
+
+  if (n_steps > 0) issue(0, 0);
+  wait_all_loads();
+  __syncthreads();
+  int ba = 0;  // buffer of tile st
+  for (int st = 0; st <= n_steps; ++st) {
+    const int bn = ba == 2 ? 0 : ba + 1;  // tile st + 1
+    const int bp = ba == 0 ? 2 : ba - 1;  // tile st - 1
+    if (st + 1 < n_steps) issue(st + 1, bn);
+    if (pw) {
+      if (st < n_steps) tile_p(st, ba, &sP[st & 1][kw][0][0][0]);
+    } else if (st >= 1) {
+      tile_ds(st - 1, bp, &sP[(st - 1) & 1][kw][0][0][0]);
+    }
+    wait_all_loads();
+    __syncthreads();  // tile st's P and tile st + 1's Q, dO published; tile st - 1 free
+    ba = bn;
+  }
+
+  // ---- epilogue: dV = acc (P wave), dK = scale * acc (dS wave); lane (c, h)
+  // holds dims 32mb + 8jj + 4h .. +3 of key c
+  if (key_ok) {
+    __bf16* op = pw ? (__bf16*)p.dv + b * p.dv_sb + (int64_t)key * p.dv_ss + hkv * p.dv_sh
+                    : (__bf16*)p.dk + b * p.dk_sb + (int64_t)key * p.dk_ss + hkv * p.dk_sh;
+    const float sc = pw ? 1.f : p.scale;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x16& a = acc[mb];
+        *(bf16x4*)(op + 32 * mb + 8 * jj + 4 * h) =
+            cvt4(a[4 * jj] * sc, a[4 * jj + 1] * sc, a[4 * jj + 2] * sc, a[4 * jj + 3] * sc);
       }
   }
 }
@@ -626,11 +969,11 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
   auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
   auto fast = [&](const __bf16* sk, const __bf16* sv) __attribute__((always_inline)) {
     auto sc_op = [&](int kb, int i) __attribute__((always_inline)) {
-      return (i & 1) ? row_frag<D, false>(sv, kb, i >> 1, qc, h) : row_frag<D, true>(sk, kb, i >> 1, qc, h);
+      return (i & 1) ? row_frag<D, SW_K>(sv, kb, i >> 1, qc, h) : row_frag<D, SW_V>(sk, kb, i >> 1, qc, h);
     };
     // gradient product i of block kb: step u = 2 kb + i / MB, column block i % MB
     auto gr_op = [&](int kb, int i) __attribute__((always_inline)) {
-      return tr_frag<D>(sk, 2 * kb + i / MB, i % MB, tr_row, tr_ch, tr_half);
+      return tr_frag<D, SW_V>(sk, 2 * kb + i / MB, i % MB, tr_row, tr_ch, tr_half);
     };
     f32x16 sb[2], db[2];
     auto sm_step = [&](int kb, int j) __attribute__((always_inline)) {
@@ -725,8 +1068,8 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
       dp[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        s[kb] = mfma32(row_frag<D, true>(sk, kb, ks, qc, h), qf[ks], s[kb]);
-        dp[kb] = mfma32(row_frag<D, false>(sv, kb, ks, qc, h), gf[ks], dp[kb]);
+        s[kb] = mfma32(row_frag<D, SW_V>(sk, kb, ks, qc, h), qf[ks], s[kb]);
+        dp[kb] = mfma32(row_frag<D, SW_K>(sv, kb, ks, qc, h), gf[ks], dp[kb]);
       }
     }
     // block mask, mixed region: the tile's 64 keys span at most five key
@@ -767,7 +1110,7 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
                              sb[o8 + 6], sb[o8 + 7]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        acc[mb] = mfma32(tr_frag<D>(sk, u, mb, tr_row, tr_ch, tr_half), df, acc[mb]);
+        acc[mb] = mfma32(tr_frag<D, SW_V>(sk, u, mb, tr_row, tr_ch, tr_half), df, acc[mb]);
     }
   };
 
@@ -805,8 +1148,13 @@ hipError_t launch(const BwdParams& p, hipStream_t s) {
                        s, p);
   }
   const int64_t nkw = (int64_t)((p.Nk + 127) / 128) * p.B * p.Hkv;
-  if (nkw > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, BLOCK>), dim3((unsigned)nkw), dim3(64 * NW), 0, s, p);
+  if (nkw > 0) {
+    if constexpr (D == 128)
+      hipLaunchKernelGGL((bwd_dkdv_split_kernel<CAUSAL, BLOCK>), dim3((unsigned)nkw), dim3(64 * NWS), 0,
+                         s, p);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, BLOCK>), dim3((unsigned)nkw), dim3(64 * NW), 0, s, p);
+  }
   const int64_t nqw = (int64_t)((p.Nq + 127) / 128) * p.B * p.Hq;
   if (nqw > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, BLOCK>), dim3((unsigned)nqw), dim3(64 * NW), 0, s, p);
