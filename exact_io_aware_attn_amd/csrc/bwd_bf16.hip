@@ -511,9 +511,7 @@ __global__ void __launch_bounds__(64 * NWS, 2) bwd_dkdv_split_kernel(const BwdPa
   }
   const int64_t nstat = (int64_t)p.B * p.Hq * p.npad;
   const DmaRsrc rst = dma_rsrc(p.stats, (uint32_t)(2 * nstat * 4));
-  auto issue = [&](int st, int buf) {
-    const int g = st / n_qt;
-    const int r0 = tile_row(st - g * n_qt);
+  auto issue = [&](int g, int r0, int buf) {
     const int hq = hkv * G + g;
     const int nvalid = min(BT, p.Nq - r0);
     const __bf16* qb = (const __bf16*)p.q + b * p.q_sb + (int64_t)r0 * p.q_ss + hq * p.q_sh;
@@ -793,39 +791,47 @@ __global__ void __launch_bounds__(64 * NWS, 2) bwd_dkdv_split_kernel(const BwdPa
     }
   };
 
-  auto tile_p = [&](int st, int buf, bf16x8* pdst) {
-    const int g = st / n_qt;
-    const int r0 = tile_row(st - g * n_qt);
+  auto tile_p = [&](int r0, int buf, bf16x8* pdst) {
     int state[2];
     states(r0, state);
     if (state[0] == 1 && state[1] == 1) p_fast(sQ[buf], sG[buf], sSt[buf], pdst);
     else p_general(r0, state, sQ[buf], sG[buf], sSt[buf], pdst);
   };
-  auto tile_ds = [&](int st, int buf, const bf16x8* psrc) {
-    const int g = st / n_qt;
-    const int r0 = tile_row(st - g * n_qt);
+  auto tile_ds = [&](int r0, int buf, const bf16x8* psrc) {
     int state[2];
     states(r0, state);
     if (state[0] == 1 && state[1] == 1) ds_fast(sQ[buf], sG[buf], sSt[buf], psrc);
     else ds_general(state, sQ[buf], sG[buf], sSt[buf], psrc);
   };
 
-  if (n_steps > 0) issue(0, 0);
+  // step s: query head hkv*G + s / n_qt, tile s % n_qt, tracked as
+  // (head, tile index) for steps st - 1, st and st + 1
+  if (n_steps > 0) issue(0, tile_row(0), 0);
   wait_all_loads();
   __syncthreads();
-  int ba = 0;  // buffer of tile st
+  int ba = 0;          // buffer of tile st
+  int ic = 0, ip = 0;  // tile index of steps st and st - 1
+  int gc = 0;          // query head of step st
   for (int st = 0; st <= n_steps; ++st) {
     const int bn = ba == 2 ? 0 : ba + 1;  // tile st + 1
     const int bp = ba == 0 ? 2 : ba - 1;  // tile st - 1
-    if (st + 1 < n_steps) issue(st + 1, bn);
+    int in = ic + 1, gn = gc;
+    if (in == n_qt) {
+      in = 0;
+      ++gn;
+    }
+    if (st + 1 < n_steps) issue(gn, tile_row(in), bn);
     if (pw) {
-      if (st < n_steps) tile_p(st, ba, &sP[st & 1][kw][0][0][0]);
+      if (st < n_steps) tile_p(tile_row(ic), ba, &sP[st & 1][kw][0][0][0]);
     } else if (st >= 1) {
-      tile_ds(st - 1, bp, &sP[(st - 1) & 1][kw][0][0][0]);
+      tile_ds(tile_row(ip), bp, &sP[(st - 1) & 1][kw][0][0][0]);
     }
     wait_all_loads();
     __syncthreads();  // tile st's P and tile st + 1's Q, dO published; tile st - 1 free
     ba = bn;
+    ip = ic;
+    ic = in;
+    gc = gn;
   }
 
   // ---- epilogue: dV = acc (P wave), dK = scale * acc (dS wave); lane (c, h)
