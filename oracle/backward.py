@@ -19,7 +19,10 @@ Reading taken here: the backward pass returns the exact gradient of
 O = softmax(scale * Q K^T + mask) V with respect to Q, K and V, for an upstream
 gradient dO, by the chain rule; nothing else is plausible for an exact method.
 With GQA a K/V head's gradient is the sum over the query heads that read it.
-Masked pairs have P = 0 and receive no gradient.
+Masked pairs have P = 0 and receive no gradient. Each gradient is a sum over
+the allowed (row, key) pairs only, so a value at a pair the mask hides (an
+Inf or NaN included) is no term of any gradient -- the forward oracle's
+reading carried through the chain rule.
 """
 
 import numpy as np
@@ -27,6 +30,21 @@ import numpy as np
 from .attention import _check_heads, element_mask
 
 _ROW_CHUNK = 2048
+
+
+def _pair_sum(W, X, allowed):
+    """R[i] = sum over j with allowed[i, j] of W[i, j] * X[j], where W is 0 at
+    the pairs that are not allowed. With X finite this is W @ X; an Inf or NaN
+    entry X[j, c] is added only to the rows i allowed to pair with j (a zero
+    weight times it would otherwise make every row NaN)."""
+    fin = np.isfinite(X)
+    if fin.all():
+        return W @ X
+    R = W @ np.where(fin, X, 0.0)
+    for j, c in zip(*np.nonzero(~fin)):
+        a = allowed[:, j]
+        R[a, c] += W[a, j] * X[j, c]
+    return R
 
 
 def attention_backward(q, k, v, do, scale, *, causal=False, block_mask=None,
@@ -44,6 +62,9 @@ def attention_backward(q, k, v, do, scale, *, causal=False, block_mask=None,
     3. Softmax Jacobian per row: dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik).
     4. S is linear in Q and K:  dQ = scale * dS K  and  dK = scale * dS^T Q.
     5. GQA: dK and dV of a K/V head accumulate over its query heads.
+    Every sum in 2-4 runs over the allowed pairs only: dP and dS are 0 at the
+    other pairs, and the three products add a non-finite operand entry only
+    through allowed pairs (_pair_sum).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -72,11 +93,11 @@ def attention_backward(q, k, v, do, scale, *, causal=False, block_mask=None,
                 m = np.where(live, S.max(axis=1), 0.0)
                 P = np.where(allowed, np.exp(S - m[:, None]), 0.0)
                 l = P.sum(axis=1)
-                P = P / np.where(live, l, 1.0)[:, None]
+                P = np.where(allowed, P / np.where(live, l, 1.0)[:, None], 0.0)
                 dO = do[b, rr, h, :]
-                dV[b, :, kvh, :] += P.T @ dO
-                dP = dO @ Vb.T
-                dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
-                dQ[b, rr, h, :] = scale * (dS @ Kb)
-                dK[b, :, kvh, :] += scale * (dS.T @ q[b, rr, h, :])
+                dV[b, :, kvh, :] += _pair_sum(P.T, dO, allowed.T)
+                dP = np.where(allowed, dO @ Vb.T, 0.0)
+                dS = np.where(allowed, P * (dP - (P * dP).sum(axis=1, keepdims=True)), 0.0)
+                dQ[b, rr, h, :] = scale * _pair_sum(dS, Kb, allowed)
+                dK[b, :, kvh, :] += scale * _pair_sum(dS.T, q[b, rr, h, :], allowed.T)
     return dQ, dK, dV

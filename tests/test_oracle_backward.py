@@ -180,3 +180,68 @@ def test_finite_differences_reject_planted_mistakes(mistake):
     ok = all(np.allclose(g, f[0, :, 0], rtol=1e-6, atol=1e-8)
              for g, f in ((dq, fq), (dk, fk), (dv, fv)))
     assert ok == (mistake == "none")  # the unplanted copy is the control
+
+
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")  # NaN/Inf inputs on purpose
+def test_values_at_hidden_pairs_are_no_term_of_any_gradient():
+    """An Inf or NaN planted where the mask hides it from part of the rows
+    leaves every gradient entry that has no allowed path to it exactly as with
+    a finite value there; entries reached through an allowed pair propagate it
+    (IEEE). Paths worked out by hand from the chain rule, causal with
+    Nq != Nk (row q sees keys <= q + 3) and a 3 x 3 block mask."""
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((1, 12, 2, 8))
+    k = rng.standard_normal((1, 15, 1, 8))
+    v = rng.standard_normal((1, 15, 1, 8))
+    do = rng.standard_normal((1, 12, 2, 8))
+    rows = np.arange(12)
+    keys = np.arange(15)
+    base = oracle.attention_backward(q, k, v, do, 0.3, causal=True)
+
+    def run(**planted):
+        t = {"q": q, "k": k, "v": v, "do": do}
+        for name, (idx, val) in planted.items():
+            t[name] = t[name].copy()
+            t[name][idx] = val
+        return oracle.attention_backward(t["q"], t["k"], t["v"], t["do"], 0.3, causal=True)
+
+    for bad in (np.nan, np.inf):
+        # V at key 9 (seen by rows >= 6): dV never involves V; rows < 6 never meet it
+        dQ, dK, dV = run(v=((0, 9, 0, slice(None)), bad))
+        assert np.array_equal(dV, base[2])
+        assert np.array_equal(dQ[0, rows < 6], base[0][0, rows < 6])
+        assert not np.isfinite(dQ[0, rows >= 6]).any()
+        # dO at row 4 (sees keys <= 7)
+        dQ, dK, dV = run(do=((0, 4, 0, slice(None)), bad))
+        assert np.array_equal(dV[0, keys > 7], base[2][0, keys > 7])
+        assert np.array_equal(dK[0, keys > 7], base[1][0, keys > 7])
+        assert np.array_equal(dQ[0, rows != 4], base[0][0, rows != 4])
+        assert np.array_equal(dQ[0, 4, 1], base[0][0, 4, 1])  # the other query head
+        assert not np.isfinite(dQ[0, 4, 0]).any() and not np.isfinite(dV[0, keys <= 7]).any()
+        # K at key 9: rows < 6 never meet it
+        dQ, dK, dV = run(k=((0, 9, 0, slice(None)), bad))
+        assert np.array_equal(dQ[0, rows < 6], base[0][0, rows < 6])
+        assert not np.isfinite(dQ[0, rows >= 6]).any()
+        # Q at row 4: keys > 7 never meet it
+        dQ, dK, dV = run(q=((0, 4, 1, slice(None)), bad))
+        assert np.array_equal(dK[0, keys > 7], base[1][0, keys > 7])
+        assert np.array_equal(dV[0, keys > 7], base[2][0, keys > 7])
+        assert np.array_equal(dQ[0, rows != 4], base[0][0, rows != 4])
+        assert not np.isfinite(dK[0, keys <= 7]).any()
+
+    # block mask: key block 1 (keys 5..9) is seen by block rows 1 and 2 (rows 4..11)
+    bm = np.array([[1, 0, 1], [0, 1, 1], [1, 1, 0]], dtype=np.uint8)
+    kw = dict(block_mask=bm, block_q=4, block_k=5)
+    b0 = oracle.attention_backward(q, k, v, do, 0.5, **kw)
+    vb = v.copy()
+    vb[0, 7, 0, 2] = np.nan
+    dQ, dK, dV = oracle.attention_backward(q, k, vb, do, 0.5, **kw)
+    assert np.array_equal(dV, b0[2])
+    assert np.array_equal(dQ[0, rows < 4], b0[0][0, rows < 4])
+    assert not np.isfinite(dQ[0, rows >= 4]).any()
+    dob = do.copy()
+    dob[0, 1, 0, :] = np.inf  # block row 0 sees key blocks 0 and 2
+    dQ, dK, dV = oracle.attention_backward(q, k, v, dob, 0.5, **kw)
+    assert np.array_equal(dV[0, 5:10], b0[2][0, 5:10])
+    assert np.array_equal(dK[0, 5:10], b0[1][0, 5:10])
+    assert not np.isfinite(dV[0, :5]).any() and not np.isfinite(dV[0, 10:]).any()
