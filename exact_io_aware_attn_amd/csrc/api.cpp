@@ -375,7 +375,8 @@ int attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq) {
   if (B < 0 || Hq <= 0 || Nq < 0) return 0;
   const size_t npad = (size_t)(Nq + 63) / 64 * 64;
-  return align_up(2 * (size_t)B * Hq * npad * sizeof(float));
+  const size_t stats = align_up(2 * (size_t)B * Hq * npad * sizeof(float));
+  return stats > 0 ? stats + align_up(sizeof(int)) : 0;
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -450,6 +451,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   p.nkb = block ? Nk / block_k : 0;
   p.npad = (Nq + 63) / 64 * 64;
   p.stats = (float*)workspace;
+  p.flag = need > 0 ? (int*)((char*)workspace + align_up(2 * (size_t)B * Hq * p.npad * sizeof(float)))
+                    : nullptr;
   hipError_t e = miattn::launch_bwd_bf16(p, d, (mask_kind & MIATTN_MASK_CAUSAL) != 0, block,
                                          (hipStream_t)stream);
   return e == hipSuccess ? MIATTN_OK : MIATTN_ERR_HIP;

@@ -128,6 +128,126 @@ __device__ int live_tiles(const BwdParams& p, int t_begin, int t_end, int s0, in
   return count;
 }
 
+// ---- Exact recomputation of gradient rows that turned non-finite. In a
+// tile the masks cut, an excluded pair has weight 0, and 0 times an Inf or
+// NaN operand (Q or dO of a row a key cannot reach, K of a key a row cannot
+// see) is NaN in the matrix products. The main kernels raise a flag in the
+// workspace when a wave's accumulators are non-finite; bwd_fix_kernel then
+// recomputes every gradient row holding an Inf or NaN with sums over the
+// visible pairs only, so such a value is no term of any gradient and values
+// at visible pairs propagate as IEEE arithmetic does. Lanes split the head
+// dimension (D / 64 elements each); each dot product is summed over the wave.
+
+// dK and dV of one key of one (batch, KV head)
+template <int D, bool CAUSAL, bool BLOCK>
+__device__ void exact_key_row(const BwdParams& p, int b, int hkv, int key) {
+  constexpr int DL = D / 64;
+  const int e0 = DL * (threadIdx.x & 63);
+  const int G = p.Hq / p.Hkv;
+  const int64_t nstat = (int64_t)p.B * p.Hq * p.npad;
+  const __bf16* kr = (const __bf16*)p.k + b * p.k_sb + (int64_t)key * p.k_ss + hkv * p.k_sh + e0;
+  const __bf16* vr = (const __bf16*)p.v + b * p.v_sb + (int64_t)key * p.v_ss + hkv * p.v_sh + e0;
+  float kv[DL], vv[DL], ak[DL], av[DL];
+#pragma unroll
+  for (int e = 0; e < DL; ++e) {
+    kv[e] = bf2f(kr[e]);
+    vv[e] = bf2f(vr[e]);
+    ak[e] = av[e] = 0.f;
+  }
+  const int q_lo = CAUSAL ? max(0, key - p.causal_off) : 0;
+  for (int g = 0; g < G; ++g) {
+    const int hq = hkv * G + g;
+    const float* st = p.stats + ((int64_t)b * p.Hq + hq) * p.npad;
+    const __bf16* qh = (const __bf16*)p.q + b * p.q_sb + hq * p.q_sh + e0;
+    const __bf16* gh = (const __bf16*)p.dout + b * p.do_sb + hq * p.do_sh + e0;
+    for (int q = q_lo; q < p.Nq; ++q) {
+      if (BLOCK && p.block_mask[(int64_t)(q / p.block_q) * p.nkb + key / p.block_k] == 0) continue;
+      float qv[DL], gv[DL], sd = 0.f, dd = 0.f;
+#pragma unroll
+      for (int e = 0; e < DL; ++e) {
+        qv[e] = bf2f(qh[(int64_t)q * p.q_ss + e]);
+        gv[e] = bf2f(gh[(int64_t)q * p.do_ss + e]);
+        sd = __builtin_fmaf(qv[e], kv[e], sd);
+        dd = __builtin_fmaf(gv[e], vv[e], dd);
+      }
+      sd = wave_sum(sd);
+      dd = wave_sum(dd);
+      const float pr = ex2(__builtin_fmaf(sd, p.scale_log2, -st[q]));
+      const float ds = pr * (dd - st[nstat + q]);
+#pragma unroll
+      for (int e = 0; e < DL; ++e) {
+        av[e] = __builtin_fmaf(pr, gv[e], av[e]);
+        ak[e] = __builtin_fmaf(ds, qv[e], ak[e]);
+      }
+    }
+  }
+  __bf16* dkr = (__bf16*)p.dk + b * p.dk_sb + (int64_t)key * p.dk_ss + hkv * p.dk_sh + e0;
+  __bf16* dvr = (__bf16*)p.dv + b * p.dv_sb + (int64_t)key * p.dv_ss + hkv * p.dv_sh + e0;
+#pragma unroll
+  for (int e = 0; e < DL; ++e) {
+    dkr[e] = (__bf16)(ak[e] * p.scale);
+    dvr[e] = (__bf16)av[e];
+  }
+}
+
+// dQ of one query row of one (batch, query head)
+template <int D, bool CAUSAL, bool BLOCK>
+__device__ void exact_q_row(const BwdParams& p, int b, int hq, int q) {
+  constexpr int DL = D / 64;
+  const int e0 = DL * (threadIdx.x & 63);
+  const int hkv = hq / (p.Hq / p.Hkv);
+  const int64_t nstat = (int64_t)p.B * p.Hq * p.npad;
+  const int64_t srow = ((int64_t)b * p.Hq + hq) * p.npad + q;
+  const __bf16* qr = (const __bf16*)p.q + b * p.q_sb + (int64_t)q * p.q_ss + hq * p.q_sh + e0;
+  const __bf16* gr = (const __bf16*)p.dout + b * p.do_sb + (int64_t)q * p.do_ss + hq * p.do_sh + e0;
+  const __bf16* kh = (const __bf16*)p.k + b * p.k_sb + hkv * p.k_sh + e0;
+  const __bf16* vh = (const __bf16*)p.v + b * p.v_sb + hkv * p.v_sh + e0;
+  float qv[DL], gv[DL], aq[DL];
+#pragma unroll
+  for (int e = 0; e < DL; ++e) {
+    qv[e] = bf2f(qr[e]);
+    gv[e] = bf2f(gr[e]);
+    aq[e] = 0.f;
+  }
+  const float lse2 = p.stats[srow], dsum = p.stats[nstat + srow];
+  const int k_hi = CAUSAL ? min(p.Nk, q + p.causal_off + 1) : p.Nk;
+  for (int key = 0; key < k_hi; ++key) {
+    if (BLOCK && p.block_mask[(int64_t)(q / p.block_q) * p.nkb + key / p.block_k] == 0) continue;
+    float kv[DL], sd = 0.f, dd = 0.f;
+#pragma unroll
+    for (int e = 0; e < DL; ++e) {
+      kv[e] = bf2f(kh[(int64_t)key * p.k_ss + e]);
+      sd = __builtin_fmaf(qv[e], kv[e], sd);
+      dd = __builtin_fmaf(gv[e], bf2f(vh[(int64_t)key * p.v_ss + e]), dd);
+    }
+    sd = wave_sum(sd);
+    dd = wave_sum(dd);
+    const float ds = ex2(__builtin_fmaf(sd, p.scale_log2, -lse2)) * (dd - dsum);
+#pragma unroll
+    for (int e = 0; e < DL; ++e) aq[e] = __builtin_fmaf(ds, kv[e], aq[e]);
+  }
+  __bf16* dqr = (__bf16*)p.dq + b * p.dq_sb + (int64_t)q * p.dq_ss + hq * p.dq_sh + e0;
+#pragma unroll
+  for (int e = 0; e < DL; ++e) dqr[e] = (__bf16)(aq[e] * p.scale);
+}
+
+// A gradient row (D / 64 elements per lane) holds an Inf or NaN.
+template <int D>
+__device__ __forceinline__ bool row_nonfinite(const __bf16* r) {
+  constexpr int DL = D / 64;
+  bool bad = false;
+#pragma unroll
+  for (int e = 0; e < DL; ++e) bad |= !__builtin_isfinite(bf2f(r[DL * (threadIdx.x & 63) + e]));
+  return __ballot(bad) != 0;
+}
+
+// Raised by each lane that wrote an Inf or NaN (a vector store under the
+// lanes' own condition; a ballot first cost the d = 64 dK/dV kernel ten
+// registers and its third wave per SIMD)
+__device__ __forceinline__ void raise_flag(const BwdParams& p, bool nonfinite) {
+  if (nonfinite) *p.flag = 1;
+}
+
 // ---- D_i = dO_i . O_i (fp32) and LSE_i * log2(e), per (batch, head, row);
 // rows Nq .. npad-1 get D = 0 and +inf (their weights exp2(s - inf) are 0).
 // D/8 lanes per row, 16 bytes each.
@@ -138,6 +258,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const BwdParams p) {
   const int64_t total = (int64_t)p.B * p.Hq * p.npad;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   const int ch = threadIdx.x % LPR;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *p.flag = 0;
   if (row >= total) return;  // whole groups of LPR lanes leave together
   const int i = (int)(row % p.npad);
   const int64_t bh = row / p.npad;
@@ -401,6 +522,9 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dkdv_kernel(const BwdParams p)
 
   // ---- epilogue: dK = scale * acc, dV = acc; lane (c, h) holds dims
   // 32mb + 8jj + 4h .. +3 of key c
+  // with masks, an Inf or NaN written here raises the flag (bwd_fix_kernel):
+  // x * 0 is 0 for finite x and NaN otherwise
+  float nf = 0.f;
   if (key_ok) {
     __bf16* dkp = (__bf16*)p.dk + b * p.dk_sb + (int64_t)key * p.dk_ss + hkv * p.dk_sh;
     __bf16* dvp = (__bf16*)p.dv + b * p.dv_sb + (int64_t)key * p.dv_ss + hkv * p.dv_sh;
@@ -410,6 +534,9 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dkdv_kernel(const BwdParams p)
       for (int jj = 0; jj < 4; ++jj) {
         const f32x16& a = dkacc[mb];
         const f32x16& v = dvacc[mb];
+        if constexpr (CAUSAL || BLOCK)
+          for (int i = 0; i < 4; ++i)
+            nf = __builtin_fmaf(a[4 * jj + i], 0.f, __builtin_fmaf(v[4 * jj + i], 0.f, nf));
         *(bf16x4*)(dkp + 32 * mb + 8 * jj + 4 * h) =
             cvt4(a[4 * jj] * p.scale, a[4 * jj + 1] * p.scale, a[4 * jj + 2] * p.scale,
                  a[4 * jj + 3] * p.scale);
@@ -417,6 +544,7 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dkdv_kernel(const BwdParams p)
             cvt4(v[4 * jj], v[4 * jj + 1], v[4 * jj + 2], v[4 * jj + 3]);
       }
   }
+  if constexpr (CAUSAL || BLOCK) raise_flag(p, nf != 0.f);
 }
 
 // ---- dK and dV at d = 128 with each 32-key block's work split over two
@@ -836,6 +964,9 @@ __global__ void __launch_bounds__(64 * NWS, 2) bwd_dkdv_split_kernel(const BwdPa
 
   // ---- epilogue: dV = acc (P wave), dK = scale * acc (dS wave); lane (c, h)
   // holds dims 32mb + 8jj + 4h .. +3 of key c
+  // with masks, an Inf or NaN written here raises the flag (bwd_fix_kernel):
+  // x * 0 is 0 for finite x and NaN otherwise
+  float nf = 0.f;
   if (key_ok) {
     __bf16* op = pw ? (__bf16*)p.dv + b * p.dv_sb + (int64_t)key * p.dv_ss + hkv * p.dv_sh
                     : (__bf16*)p.dk + b * p.dk_sb + (int64_t)key * p.dk_ss + hkv * p.dk_sh;
@@ -845,10 +976,13 @@ __global__ void __launch_bounds__(64 * NWS, 2) bwd_dkdv_split_kernel(const BwdPa
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const f32x16& a = acc[mb];
+        if constexpr (CAUSAL || BLOCK)
+          for (int i = 0; i < 4; ++i) nf = __builtin_fmaf(a[4 * jj + i], 0.f, nf);
         *(bf16x4*)(op + 32 * mb + 8 * jj + 4 * h) =
             cvt4(a[4 * jj] * sc, a[4 * jj + 1] * sc, a[4 * jj + 2] * sc, a[4 * jj + 3] * sc);
       }
   }
+  if constexpr (CAUSAL || BLOCK) raise_flag(p, nf != 0.f);
 }
 
 // ---- dQ. Workgroup: 128 query rows of one (batch, query head); wave w holds
@@ -1131,6 +1265,9 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
     __syncthreads();
   }
 
+  // with masks, an Inf or NaN written here raises the flag (bwd_fix_kernel):
+  // x * 0 is 0 for finite x and NaN otherwise
+  float nf = 0.f;
   if (row_ok) {
     __bf16* op = (__bf16*)p.dq + b * p.dq_sb + (int64_t)qrow * p.dq_ss + hq * p.dq_sh;
 #pragma unroll
@@ -1138,10 +1275,43 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const f32x16& a = acc[mb];
+        if constexpr (CAUSAL || BLOCK)
+          for (int e = 0; e < 4; ++e) nf = __builtin_fmaf(a[4 * jj + e], 0.f, nf);
         *(bf16x4*)(op + 32 * mb + 8 * jj + 4 * h) =
             cvt4(a[4 * jj] * p.scale, a[4 * jj + 1] * p.scale, a[4 * jj + 2] * p.scale,
                  a[4 * jj + 3] * p.scale);
       }
+  }
+  if constexpr (CAUSAL || BLOCK) raise_flag(p, nf != 0.f);
+}
+
+// ---- After the main kernels, with masks only: nothing unless a wave raised
+// the flag; then every gradient row holding an Inf or NaN is recomputed
+// exactly (one wave per row, rows strided over the grid: the keys' dK and dV
+// rows first, then the query rows' dQ).
+template <int D, bool CAUSAL, bool BLOCK>
+__global__ void __launch_bounds__(256) bwd_fix_kernel(const BwdParams p) {
+  if (__atomic_load_n(p.flag, __ATOMIC_RELAXED) == 0) return;
+  const int64_t nkeys = (int64_t)p.B * p.Hkv * p.Nk;
+  const int64_t total = nkeys + (int64_t)p.B * p.Hq * p.Nq;
+  const int64_t stride = (int64_t)gridDim.x * (blockDim.x / 64);
+  for (int64_t r = (int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64; r < total; r += stride) {
+    if (r < nkeys) {
+      const int key = (int)(r % p.Nk);
+      const int bh = (int)(r / p.Nk);
+      const int b = bh / p.Hkv, hkv = bh % p.Hkv;
+      const __bf16* dkr = (const __bf16*)p.dk + b * p.dk_sb + (int64_t)key * p.dk_ss + hkv * p.dk_sh;
+      const __bf16* dvr = (const __bf16*)p.dv + b * p.dv_sb + (int64_t)key * p.dv_ss + hkv * p.dv_sh;
+      const bool bad_k = row_nonfinite<D>(dkr), bad_v = row_nonfinite<D>(dvr);
+      if (bad_k || bad_v) exact_key_row<D, CAUSAL, BLOCK>(p, b, hkv, key);
+    } else {
+      const int64_t rq = r - nkeys;
+      const int q = (int)(rq % p.Nq);
+      const int bh = (int)(rq / p.Nq);
+      const int b = bh / p.Hq, hq = bh % p.Hq;
+      const __bf16* dqr = (const __bf16*)p.dq + b * p.dq_sb + (int64_t)q * p.dq_ss + hq * p.dq_sh;
+      if (row_nonfinite<D>(dqr)) exact_q_row<D, CAUSAL, BLOCK>(p, b, hq, q);
+    }
   }
 }
 
@@ -1164,6 +1334,9 @@ hipError_t launch(const BwdParams& p, hipStream_t s) {
   const int64_t nqw = (int64_t)((p.Nq + 127) / 128) * p.B * p.Hq;
   if (nqw > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, BLOCK>), dim3((unsigned)nqw), dim3(64 * NW), 0, s, p);
+  // the flag lives in the workspace, which exists when there are query rows
+  if ((CAUSAL || BLOCK) && rows > 0)
+    hipLaunchKernelGGL((bwd_fix_kernel<D, CAUSAL, BLOCK>), dim3(256), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -107,6 +107,7 @@ struct BwdParams {
   int block_q, block_k, nkb;
   int npad;           // Nq rounded up to 64
   float* stats;       // [2][B*Hq][npad]: lse * log2(e) (+inf past Nq), rowsum(dO * O) (0 past Nq)
+  int* flag;          // in the workspace after stats: set when a gradient accumulator turned non-finite
 };
 
 constexpr int kMaxSplits = 4096;

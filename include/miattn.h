@@ -251,7 +251,8 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
 
 /* Bytes of device workspace attn_bwd needs: two fp32 rows of Nq rounded up
  * to 64 per (batch, query head) -- the forward LSE in base-2 units and
- * D_i = dO_i . O_i. Returns 0 for invalid sizes. */
+ * D_i = dO_i . O_i -- then a 256-byte slot holding a flag. 0 when Nq is 0
+ * and for invalid sizes. */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
 
 /* Backward pass by recomputation ("플래시어텐션: 메모리를 아끼는 정확한 어텐션",
@@ -280,6 +281,11 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
  *             owned by the caller, overwritten by the call
  * stream      hipStream_t
  * A query row with no visible key gets dQ = 0 and adds nothing to dK, dV.
+ * Inf or NaN in an input reaches only the gradient entries that a pair the
+ * mask allows connects it to: with a mask, a wave whose accumulators turn
+ * non-finite sets the workspace flag, and a last kernel then recomputes
+ * every gradient row holding an Inf or NaN from the visible pairs alone
+ * (slow; only on that path).
  * Outputs must not overlap the inputs. */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, int dtype, int B, int Hq,

@@ -115,6 +115,18 @@ def check_grad(g_gpu, G_ref, where=""):
     return rel, rmax
 
 
+def check_grad_nonfinite(g_gpu, G_ref, where=""):
+    """A gradient of inputs holding Inf/NaN values: non-finite entries exactly
+    where the oracle has them (the entries an allowed pair connects to such a
+    value), the finite rest within the gradient band."""
+    g = to64(g_gpu)
+    bad_g, bad_ref = ~np.isfinite(g), ~np.isfinite(G_ref)
+    assert np.array_equal(bad_g, bad_ref), (
+        f"{where}: {int((bad_g & ~bad_ref).sum())} non-finite entries the oracle has finite, "
+        f"{int((bad_ref & ~bad_g).sum())} the other way")
+    return check_grad(np.where(bad_g, 0.0, g), np.where(bad_ref, 0.0, G_ref), where=where)
+
+
 def sample_rows(n, tile=128, extra=16, seed=0, boundaries=()):
     """First and last rows, rows around every tile edge up to a cap, the given
     boundaries (and their neighbours), plus random rows -- sorted, unique."""

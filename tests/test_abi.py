@@ -153,9 +153,10 @@ def test_decode_noalloc_validation(kw, status):
 
 
 def test_bwd_workspace_size():
-    # two fp32 rows of Nq rounded up to 64 per (batch, query head)
-    assert bd.attn_bwd_workspace_bytes(2, 4, 100) == 2 * 2 * 4 * 128 * 4
-    assert bd.attn_bwd_workspace_bytes(1, 32, 8192) == 2 * 32 * 8192 * 4
+    # two fp32 rows of Nq rounded up to 64 per (batch, query head), then one
+    # 256-byte slot for the non-finite flag
+    assert bd.attn_bwd_workspace_bytes(2, 4, 100) == 2 * 2 * 4 * 128 * 4 + 256
+    assert bd.attn_bwd_workspace_bytes(1, 32, 8192) == 2 * 32 * 8192 * 4 + 256
     assert bd.attn_bwd_workspace_bytes(-1, 4, 100) == 0
     assert bd.attn_bwd_workspace_bytes(2, 4, 0) == 0
 

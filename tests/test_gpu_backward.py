@@ -16,7 +16,7 @@ from exact_io_aware_attn_amd import attn_bwd, attn_fwd, prepare_bwd
 from exact_io_aware_attn_amd.inputs import (WORKLOADS, backward_inputs, frame_block_mask,
                                             workload_inputs)
 
-from parity import check_grad, to64
+from parity import check_grad, check_grad_nonfinite, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -184,3 +184,61 @@ def test_bwd_video_workload_one_head():
     got = (dq[:, :, h:h + 1], dk[:, :, h:h + 1], dv[:, :, h:h + 1])
     errs = [check_grad(g, r, f"video head {h} d{n}") for g, r, n in zip(got, ref, "QKV")]
     print("video", h, " ".join(f"d{n} {e[0]:.2e}/{e[1]:.2e}" for n, e in zip("QKV", errs)))
+
+
+# Inf/NaN planted where the mask hides it from part of the rows: (tensor,
+# index [b, row or key, head, dim] or None for every dim). Row 70 sees keys
+# up to 102 and key 180 is seen from row 148 on (Nq = 200, Nk = 232).
+_PLANTS = [("v", (0, 180, 1, 5)), ("do", (0, 70, 2, 9)), ("k", (0, 180, 1, None)),
+           ("q", (0, 70, 3, None))]
+
+
+def _planted(d, seed, plants, bad, Nq=200, Nk=232):
+    q, k, v, do = backward_inputs(1, 4, 2, Nq, Nk, d, torch.bfloat16, seed=seed)
+    t = {"q": q, "k": k, "v": v, "do": do}
+    for name, (b, r, hh, e) in plants:
+        t[name][b, r, hh, slice(None) if e is None else e] = bad
+    return t["q"], t["k"], t["v"], t["do"]
+
+
+def _check_nonfinite_grads(q, k, v, do, where, **mask):
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = attn_fwd(qd, kd, vd, **mask)
+    grads = attn_bwd(qd, kd, vd, o, lse, dod, **mask)
+    torch.cuda.synchronize()
+    okw = {kk: vv for kk, vv in mask.items() if kk in ("causal", "block_mask")}
+    if "block" in mask:
+        okw["block_q"], okw["block_k"] = mask["block"]
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = oracle.attention_backward(to64(q), to64(k), to64(v), to64(do),
+                                        1 / math.sqrt(q.shape[-1]), **okw)
+    errs = [check_grad_nonfinite(g, r, f"{where} d{n}") for g, r, n in zip(grads, ref, "QKV")]
+    print(where, " ".join(f"d{n} {e[0]:.2e}/{e[1]:.2e}" for n, e in zip("QKV", errs)))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("plant", range(len(_PLANTS)))
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_bwd_nonfinite_at_hidden_pairs(d, plant, bad):
+    """An Inf or NaN in Q, K, V or dO reaches exactly the gradient entries an
+    allowed pair connects it to, as in the oracle; rows and keys the causal
+    rule keeps away from it are unaffected (mixed tiles recompute exactly the
+    keys or rows whose accumulators turned non-finite)."""
+    name = _PLANTS[plant][0]
+    if bad == float("inf") and name in ("k", "q"):
+        pytest.skip("Inf in K or Q: the scores' signs decide; NaN covers the path")
+    q, k, v, do = _planted(d, 40 + plant, [_PLANTS[plant]], bad)
+    _check_nonfinite_grads(q, k, v, do, f"causal d={d} {name}={bad}", causal=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_nonfinite_block_mask(d, causal):
+    """The same with a block mask (blocks of 48 x 48 over 192 x 240, about half
+    live, one dead block row and column), NaN in V (key 180, block column 3)
+    and dO (row 70, block row 1)."""
+    bm = _block_mask(4, 5, seed=d + causal)
+    bm[2, 3] = bm[1, 0] = bm[1, 2] = 1
+    q, k, v, do = _planted(d, 50, [_PLANTS[0], _PLANTS[1]], float("nan"), Nq=192, Nk=240)
+    _check_nonfinite_grads(q, k, v, do, f"block c={causal} d={d}", causal=causal,
+                           block_mask=bm, block=(48, 48))
