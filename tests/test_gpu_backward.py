@@ -242,3 +242,11 @@ def test_bwd_nonfinite_block_mask(d, causal):
     q, k, v, do = _planted(d, 50, [_PLANTS[0], _PLANTS[1]], float("nan"), Nq=192, Nk=240)
     _check_nonfinite_grads(q, k, v, do, f"block c={causal} d={d}", causal=causal,
                            block_mask=bm, block=(48, 48))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_nonfinite_without_mask(d):
+    """No mask: every pair is visible, so NaN in V and dO reaches exactly the
+    entries the oracle's chain rule sends it to (no fix-up kernel runs)."""
+    q, k, v, do = _planted(d, 60, [_PLANTS[0], _PLANTS[1]], float("nan"))
+    _check_nonfinite_grads(q, k, v, do, f"no mask d={d}", causal=False)
