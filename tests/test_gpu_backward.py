@@ -250,3 +250,36 @@ def test_bwd_nonfinite_without_mask(d):
     entries the oracle's chain rule sends it to (no fix-up kernel runs)."""
     q, k, v, do = _planted(d, 60, [_PLANTS[0], _PLANTS[1]], float("nan"))
     _check_nonfinite_grads(q, k, v, do, f"no mask d={d}", causal=False)
+
+
+def _random_case(seed):
+    """A seeded random backward problem: batch 1-2, KV heads 1-2, group 1-4,
+    Nq and Nk in 1..400, d 64 or 128, causal or not, and a block mask with
+    block sizes that divide the lengths on about a third of the cases."""
+    rng = np.random.default_rng(1000 + seed)
+    B, Hkv, G = int(rng.integers(1, 3)), int(rng.integers(1, 3)), int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([64, 128]))
+    causal = bool(rng.integers(0, 2))
+    if rng.random() < 0.35:
+        bq, bk = (int(x) for x in rng.choice([16, 32, 48, 64], size=2))
+        Nq, Nk = bq * int(rng.integers(1, 7)), bk * int(rng.integers(1, 7))
+        bm = (rng.random((Nq // bq, Nk // bk)) < 0.6).astype(np.uint8)
+        return B, Hkv, G, Nq, Nk, d, causal, bm, (bq, bk)
+    Nq, Nk = int(rng.integers(1, 401)), int(rng.integers(1, 401))
+    return B, Hkv, G, Nq, Nk, d, causal, None, None
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_bwd_random_shapes(seed):
+    B, Hkv, G, Nq, Nk, d, causal, bm, blk = _random_case(seed)
+    q, k, v, do = backward_inputs(B, Hkv * G, Hkv, Nq, Nk, d, torch.bfloat16, seed=seed)
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = attn_fwd(qd, kd, vd, causal=causal, block_mask=bm, block=blk)
+    grads = attn_bwd(qd, kd, vd, o, lse, dod, causal=causal, block_mask=bm, block=blk)
+    torch.cuda.synchronize()
+    kw = {} if bm is None else dict(block_mask=bm, block_q=blk[0], block_k=blk[1])
+    ref = oracle.attention_backward(to64(q), to64(k), to64(v), to64(do), 1 / math.sqrt(d),
+                                    causal=causal, **kw)
+    where = f"seed {seed}: B={B} Hkv={Hkv} G={G} Nq={Nq} Nk={Nk} d={d} causal={causal} block={blk}"
+    errs = [check_grad(g, r, f"{where} d{n}") for g, r, n in zip(grads, ref, "QKV")]
+    print(where, " ".join(f"d{n} {e[0]:.2e}/{e[1]:.2e}" for n, e in zip("QKV", errs)))
