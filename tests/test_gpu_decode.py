@@ -278,3 +278,32 @@ def test_full_gqa_decode_b64_paged_equals_contiguous():
                                ins["seqlens"])
     torch.cuda.synchronize()
     assert torch.equal(o1, o2[:, 0]) and torch.equal(l1, l2[:, 0])
+
+
+# ------------------------------------------------------------ random problems
+@pytest.mark.parametrize("seed", range(16))
+def test_decode_random_problems(seed):
+    """Seeded random decode problems: batch 1-9, KV heads 1-4, group 1-8,
+    d 64 or 128, 1-4 new tokens (group x tokens at most 16, the library's
+    limit), lengths 0..max_len, a random split count, and every other case
+    through a paged cache (pages of 16-256 rows)."""
+    rng = np.random.default_rng(3000 + seed)
+    B, Hkv, G = int(rng.integers(1, 10)), int(rng.integers(1, 5)), int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    nt = int(rng.integers(1, min(4, 16 // G) + 1))
+    page = int(rng.choice([16, 64, 256]))
+    max_len = page * int(rng.integers(1, 9))
+    kv_splits = int(rng.choice([0, 0, 1, 3, 17]))
+    seqlens, q, kc, vc = decode_multi_inputs(B, nt, Hkv * G, Hkv, max_len, d, seed=seed, len_lo=0)
+    where = f"seed {seed}: B={B} Hkv={Hkv} G={G} d={d} nt={nt} max_len={max_len} splits={kv_splits}"
+    if seed % 2:
+        kp, vp, table = _to_pages(kc, vc, page, seed=seed)
+        o, lse = attn_decode_paged(q.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV),
+                                   seqlens.to(DEV), kv_splits=kv_splits)
+        where += f" paged {page}"
+    else:
+        o, lse = attn_decode_multi(q.to(DEV), kc.to(DEV), vc.to(DEV), seqlens.to(DEV),
+                                   kv_splits=kv_splits)
+    torch.cuda.synchronize()
+    O, L = _multi_ref(q, kc, vc, seqlens.numpy(), 1 / math.sqrt(d))
+    check(o, O, lse, L, where=where)

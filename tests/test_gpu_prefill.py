@@ -546,3 +546,38 @@ def test_bf16_fixed_max_causal_large_late_keys(mode):
     assert (f[:, :, oracle.MIN_KEYS - 1:N - 64] == 1).all()
     assert (f[:, :, N - 64:] == 0).mean() > 0.5
     check_decisions(f, q, k, mode, causal=True)
+
+
+# ------------------------------------------------------------ random problems
+def _random_fwd_case(seed):
+    """A seeded random prefill problem: batch 1-2, KV heads 1-2, group 1-4,
+    Nq and Nk in 1..600, d 64 or 128, bf16 (fp32 on a quarter of the cases),
+    causal or not, any softmax mode, and a block mask (block sizes 16-80
+    dividing the lengths, about 60 % live) on about a third of the cases."""
+    rng = np.random.default_rng(2000 + seed)
+    B, Hkv, G = int(rng.integers(1, 3)), int(rng.integers(1, 3)), int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([64, 128]))
+    dtype = torch.float32 if rng.random() < 0.25 else torch.bfloat16
+    causal = bool(rng.integers(0, 2))
+    mode = str(rng.choice(["online", "fixed_max", "fixed_max_centered"]))
+    bm = blk = None
+    if rng.random() < 0.35:
+        bq, bk = (int(x) for x in rng.choice([16, 32, 48, 64, 80], size=2))
+        Nq, Nk = bq * int(rng.integers(1, 8)), bk * int(rng.integers(1, 8))
+        bm = (rng.random((Nq // bq, Nk // bk)) < 0.6).astype(np.uint8)
+        blk = (bq, bk)
+    else:
+        Nq, Nk = int(rng.integers(1, 601)), int(rng.integers(1, 601))
+    return B, Hkv, G, Nq, Nk, d, dtype, causal, mode, bm, blk
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_fwd_random_problems(seed):
+    B, Hkv, G, Nq, Nk, d, dtype, causal, mode, bm, blk = _random_fwd_case(seed)
+    q, k, v = prefill_inputs(B, Hkv * G, Hkv, Nq, Nk, d, dtype, seed=seed)
+    o, lse = _run(q, k, v, causal=causal, block_mask=bm, block=blk, softmax=mode)
+    kw = {} if bm is None else dict(block_mask=bm, block_q=blk[0], block_k=blk[1])
+    O, L = _ref(q, k, v, 1 / math.sqrt(d), causal=causal, **kw)
+    check(o, O, lse, L, dtype="f32" if dtype == torch.float32 else "bf16",
+          where=f"seed {seed}: B={B} Hkv={Hkv} G={G} Nq={Nq} Nk={Nk} d={d} {dtype} "
+                f"causal={causal} {mode} block={blk}")
