@@ -283,3 +283,12 @@ def test_bwd_random_shapes(seed):
     where = f"seed {seed}: B={B} Hkv={Hkv} G={G} Nq={Nq} Nk={Nk} d={d} causal={causal} block={blk}"
     errs = [check_grad(g, r, f"{where} d{n}") for g, r, n in zip(grads, ref, "QKV")]
     print(where, " ".join(f"d{n} {e[0]:.2e}/{e[1]:.2e}" for n, e in zip("QKV", errs)))
+
+
+@pytest.mark.parametrize("Hq,Hkv,Nq,Nk,d,causal", [(2, 1, 512, 65536, 128, True),
+                                                   (4, 2, 300, 40000, 64, False)])
+def test_bwd_long_keys(Hq, Hkv, Nq, Nk, d, causal):
+    """Long key ranges (512 key workgroups per head, loops of up to 1024 key
+    tiles in dQ, 64-bit row offsets), every gradient entry against the oracle."""
+    _check(*backward_inputs(1, Hq, Hkv, Nq, Nk, d, torch.bfloat16, seed=Nk % 97), causal,
+           f"long keys {Hq}/{Hkv} {Nq}x{Nk} d={d} causal={causal}")
