@@ -286,9 +286,13 @@ def test_bwd_random_shapes(seed):
 
 
 @pytest.mark.parametrize("Hq,Hkv,Nq,Nk,d,causal", [(2, 1, 512, 65536, 128, True),
-                                                   (4, 2, 300, 40000, 64, False)])
+                                                   (4, 2, 300, 40000, 64, False),
+                                                   (2, 1, 65536, 512, 128, False),
+                                                   (4, 2, 40000, 300, 64, True)])
 def test_bwd_long_keys(Hq, Hkv, Nq, Nk, d, causal):
     """Long key ranges (512 key workgroups per head, loops of up to 1024 key
-    tiles in dQ, 64-bit row offsets), every gradient entry against the oracle."""
+    tiles in dQ, 64-bit row offsets) and long query ranges (up to 2048 steps
+    per key workgroup; causal with 39700 rows that see no key: dQ = 0 there),
+    every gradient entry against the oracle."""
     _check(*backward_inputs(1, Hq, Hkv, Nq, Nk, d, torch.bfloat16, seed=Nk % 97), causal,
            f"long keys {Hq}/{Hkv} {Nq}x{Nk} d={d} causal={causal}")
