@@ -1291,7 +1291,7 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
 // rows first, then the query rows' dQ).
 template <int D, bool CAUSAL, bool BLOCK>
 __global__ void __launch_bounds__(256) bwd_fix_kernel(const BwdParams p) {
-  if (__atomic_load_n(p.flag, __ATOMIC_RELAXED) == 0) return;
+  if (*(const volatile int*)p.flag == 0) return;
   const int64_t nkeys = (int64_t)p.B * p.Hkv * p.Nk;
   const int64_t total = nkeys + (int64_t)p.B * p.Hq * p.Nq;
   const int64_t stride = (int64_t)gridDim.x * (blockDim.x / 64);

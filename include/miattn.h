@@ -27,6 +27,9 @@
  *    without synchronising. MIATTN_ERR_HIP reports a launch error; faults
  *    inside kernels surface at the caller's next synchronisation.
  *  - No atomics: the same inputs and arguments give bitwise identical outputs.
+ *  - A call enqueues kernels only (no memset, copy or allocation), so it can be
+ *    captured in a HIP graph and replayed; what a call keeps in its workspace
+ *    is rewritten by its own kernels on every launch or replay.
  *  - No C++ exception crosses this interface.
  */
 #ifndef MIATTN_H
