@@ -97,3 +97,48 @@ def test_graph_bwd_replays(d):
         bad_keys = torch.isnan(dv.float()).any(dim=-1).any(dim=-1)[0]
         assert bool(bad_keys[103:].any()) is False, f"replay {i}"
         assert bool(bad_keys[:103].any()) is bool(i % 2), f"replay {i}"
+
+
+def test_graph_decode_noalloc_and_paged_replays():
+    """The allocation-free decode (static per-device scratch) and the paged
+    multi-token decode, each captured and replayed with changed lengths."""
+    import numpy as np
+    from exact_io_aware_attn_amd import (attn_decode_multi_workspace_bytes, attn_decode_noalloc,
+                                         attn_decode_paged)
+    from exact_io_aware_attn_amd.inputs import decode_multi_inputs
+
+    seqlens, q, kc, vc = decode_inputs(5, 16, 4, 1024, 64, torch.bfloat16, seed=6, len_lo=0)
+    seqlens, q, kc, vc = (x.to(DEV) for x in (seqlens, q, kc, vc))
+    o, lse = torch.empty_like(q), torch.empty((5, 16), dtype=torch.float32, device=DEV)
+    g1 = _capture(lambda: attn_decode_noalloc(q, kc, vc, seqlens, o, lse))
+
+    B, nt, Hq, Hkv, max_len, d, page = 4, 3, 8, 2, 512, 128, 64
+    sl2, q2, kc2, vc2 = decode_multi_inputs(B, nt, Hq, Hkv, max_len, d, seed=7, len_lo=0)
+    mp = max_len // page
+    perm = np.random.default_rng(7).permutation(B * mp + 2)[:B * mp].astype(np.int32)
+    table = torch.from_numpy(perm).view(B, mp)
+    kp = torch.zeros(B * mp + 2, page, Hkv, d, dtype=torch.bfloat16)
+    vp = torch.zeros_like(kp)
+    kp[table.reshape(-1).long()] = kc2.reshape(B * mp, page, Hkv, d)
+    vp[table.reshape(-1).long()] = vc2.reshape(B * mp, page, Hkv, d)
+    sl2, q2, kp, vp, table = (x.to(DEV) for x in (sl2, q2, kp, vp, table))
+    o2 = torch.empty_like(q2)
+    lse2 = torch.empty((B, nt, Hq), dtype=torch.float32, device=DEV)
+    ws = torch.empty(attn_decode_multi_workspace_bytes(B, nt, Hq, Hkv, max_len, d), dtype=torch.uint8,
+                     device=DEV)
+    g2 = _capture(lambda: attn_decode_paged(q2, kp, vp, table, sl2, out=o2, lse_out=lse2,
+                                            workspace=ws))
+    lens1 = [[1024, 0, 1, 700, 63], [3, 1024, 512, 0, 1000], [0, 0, 0, 0, 0]]
+    lens2 = [[512, 0, 2, 300], [1, 512, 511, 64], [5, 6, 7, 8]]
+    for i in range(3):
+        seqlens.copy_(torch.tensor(lens1[i], dtype=torch.int32))
+        sl2.copy_(torch.tensor(lens2[i], dtype=torch.int32))
+        torch.cuda.synchronize()
+        g1.replay()
+        g2.replay()
+        torch.cuda.synchronize()
+        e1 = attn_decode(q, kc, vc, seqlens)
+        e2 = attn_decode_paged(q2, kp, vp, table, sl2)
+        torch.cuda.synchronize()
+        assert _same(o, e1[0]) and _same(lse, e1[1]), f"noalloc replay {i}"
+        assert _same(o2, e2[0]) and _same(lse2, e2[1]), f"paged replay {i}"
