@@ -14,11 +14,14 @@ Printed (one JSON line):
              (4 d per attended query-key pair) over the prefill part of the steps
   decode     KV-read GB/s of the decode part (sum of lengths x Hkv x d x 2 x 2 B)
   roofline   prefill kernel against the dense bf16 MFMA peak (and against that peak
-             scaled to the bounds on the kernel's sustained engine clock)
-  clock      bounds on the main kernel's sustained engine clock, from a counter
-             pass of the same bench command over the kernel's time: low from
-             SQ_BUSY_CYCLES per shader engine, high from GRBM_GUI_ACTIVE per XCD;
-             stored in profiles/clock.json with a hash of the kernel sources
+             scaled to the engine clock measured under the kernel in this run)
+  clock      the engine clock the main kernel ran at, measured in this run: a
+             probe (libmiclock.so) on a second stream reads the shader-clock
+             cycle counter against the 100 MHz real-time counter on every XCD
+             while the back-to-back calls of the main part run (mean, min and
+             max over the XCDs); next to it the bracket from a stored counter
+             pass of the same command (profiles/clock.json, gated by a hash of
+             the kernel sources)
   roofline_decode  decode against the HBM peak
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample
   ms_parts_back_to_back  per part, the average of --back-to-back calls (200)
@@ -321,8 +324,20 @@ def main():
           for i in range(len(parts))]
     # after the timed steps: each part's average over back-to-back calls
     # between one pair of events (warm; no gap for the host between calls)
+    ms_avg = [sum(m) / len(m) for m in ms]
     b2b = {}
-    for p in parts:
+    live_clock = None
+    for i, p in enumerate(parts):
+        probe = None
+        # the main part's engine clock: a probe on a second stream (default
+        # priority) spans these calls but the first and last 0.5 ms
+        window_s = (args.back_to_back * ms_avg[i] - 1.0) * 1e-3
+        if i == 0 and window_s >= 1e-3:
+            from exact_io_aware_attn_amd import clock as clk_mod
+            probe = clk_mod.ClockProbe(device=dev)
+            side = torch.cuda.Stream()
+            torch.cuda.synchronize()
+            probe.start(window_s, warm_s=0.5e-3, stream=side)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.back_to_back):
@@ -330,7 +345,14 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         b2b[p.name] = e0.elapsed_time(e1) / max(args.back_to_back, 1)
-    ms_avg = [sum(m) / len(m) for m in ms]
+        if probe is not None:
+            live_clock = clk_mod.summary(probe.result())
+            live_clock.update(window_ms=window_s * 1e3, calls=args.back_to_back,
+                              source="measured in this run: shader-clock cycles (s_memtime) over "
+                                     "the 100 MHz real-time counter, one probe wave per XCD "
+                                     "(two rounds of 8) on a second stream, across the "
+                                     "back-to-back calls of the main part that follow the "
+                                     "timed steps")
     ms_step = wall * 1e3 / args.steps
 
     main_p = parts[0]
@@ -368,15 +390,17 @@ def main():
     out["ms_parts_median"] = {p.name: sorted(m)[len(m) // 2] for p, m in zip(parts, ms)}
     out["ms_parts_min"] = {p.name: min(m) for p, m in zip(parts, ms)}
     out["ms_parts_back_to_back"] = b2b
-    clk = stored_clock(main_p.name)
-    out["clock"] = clk
-    if clk is not None and roof["bound"] == "mfma":
-        # the same peak at the bounds on the engine clock the kernel held (the
-        # 2516.6 TFLOP/s figure assumes 2.4 GHz); the higher clock gives the
-        # lower fraction
-        pk = [roof["peak"] * clk[m] / 2400.0 for m in ("mhz_low", "mhz_high")]
-        roof["peak_at_sustained_clock"] = pk
-        roof["frac_at_sustained_clock"] = [roof["achieved"] / pk[1], roof["achieved"] / pk[0]]
+    out["clock"] = {"measured": live_clock, "counter_bracket": stored_clock(main_p.name)}
+    if live_clock is not None and roof["bound"] == "mfma":
+        # the same peak at the engine clock the kernel held (the 2516.6
+        # TFLOP/s figure assumes 2.4 GHz): at the mean over the XCDs, and at
+        # the slowest and fastest XCD's clock
+        pk = roof["peak"] * live_clock["mhz_mean"] / 2400.0
+        roof["peak_at_measured_clock"] = pk
+        roof["frac_at_measured_clock"] = roof["achieved"] / pk
+        rng = [roof["peak"] * live_clock[m] / 2400.0 for m in ("mhz_min", "mhz_max")]
+        roof["peak_at_xcd_clock_range"] = rng
+        roof["frac_at_xcd_clock_range"] = [roof["achieved"] / rng[1], roof["achieved"] / rng[0]]
     out["roofline"] = roof
     if len(parts) > 1 and parts[1].kind == "decode":
         d = parts[1]

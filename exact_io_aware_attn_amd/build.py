@@ -2,8 +2,10 @@
 
     python -m exact_io_aware_attn_amd.build [--jobs N]
 
-Each source under csrc/ is compiled to an object in _build/ (in parallel),
-then linked into exact_io_aware_attn_amd/libmiattn.so. Always rebuilds.
+Each attention source under csrc/ is compiled to an object in _build/ (in
+parallel), then linked into exact_io_aware_attn_amd/libmiattn.so; the engine
+clock probe (csrc/clock_probe.hip, include/miclock.h) becomes
+exact_io_aware_attn_amd/libmiclock.so. Always rebuilds.
 """
 
 import argparse
@@ -18,6 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmiattn.so")
 SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "kstats.hip", "decode.hip", "segments.hip", "bwd_bf16.hip"]
+CLOCK_LIB = os.path.join(PKG, "libmiclock.so")
+CLOCK_SOURCES = ["clock_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -39,21 +43,26 @@ def _compile(src):
     return out, msg
 
 
-def build(jobs=None, verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(_compile, SOURCES))
-    for _, msg in results:
-        if verbose and msg.strip():
-            print(msg)
-    objs = [o for o, _ in results]
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs=None, verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CLOCK_SOURCES
+    jobs = jobs or min(len(srcs), os.cpu_count() or 1)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        results = dict(zip(srcs, ex.map(_compile, srcs)))
+    for _, msg in results.values():
+        if verbose and msg.strip():
+            print(msg)
+    _link([results[s][0] for s in SOURCES], LIB)
+    _link([results[s][0] for s in CLOCK_SOURCES], CLOCK_LIB)
     return LIB
 
 

@@ -267,3 +267,35 @@ def test_product_code_does_not_use_the_oracle():
     pat = re.compile(r"^\s*(import|from)\s+oracle\b|\boracle\.", re.M)
     for f in list(root.rglob("*.py")) + list(root.rglob("*.hip")) + list(root.rglob("*.cpp")):
         assert not pat.search(f.read_text()), f
+
+
+# ---------------------------------------------------------------- clock probe
+CLOCK_HEADER = os.path.join(ROOT, "include", "miclock.h")
+
+
+@pytest.mark.skipif(not os.path.exists(os.path.join(ROOT, "exact_io_aware_attn_amd", "libmiclock.so")),
+                    reason="libmiclock.so not built")
+def test_clock_probe_library_exports_and_validates():
+    """libmiclock.so exports what include/miclock.h declares, and refuses a
+    NULL buffer or sizes out of range before launching anything."""
+    from exact_io_aware_attn_amd import clock
+    text = re.sub(r"/\*.*?\*/", "", open(CLOCK_HEADER).read(), flags=re.S)
+    names = re.findall(r"^\s*int\s+([A-Za-z_]\w*)\s*\(", text, flags=re.M)
+    assert names == ["miclock_probe"]
+    lib = clock.library()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails validation
+    assert lib.miclock_probe(None, 8, 0, 100, None) == 1
+    assert lib.miclock_probe(fake, 0, 0, 100, None) == 2
+    assert lib.miclock_probe(fake, 1025, 0, 100, None) == 2
+    assert lib.miclock_probe(fake, 8, 0, 0, None) == 2
+    assert lib.miclock_probe(fake, 8, (1 << 32) + 1, 100, None) == 2
+    assert lib.miclock_probe(fake, 8, 0, (1 << 32) + 1, None) == 2
+
+
+def test_clock_summary_groups_probes_by_xcd():
+    from exact_io_aware_attn_amd import clock
+    mhz = [2000.0 + x for x in range(8)] * 2
+    s = clock.summary(mhz)
+    assert s["mhz_per_xcd"] == [2000.0 + x for x in range(8)]
+    assert s["mhz_min"] == 2000.0 and s["mhz_max"] == 2007.0
+    assert abs(s["mhz_mean"] - 2003.5) < 1e-9
