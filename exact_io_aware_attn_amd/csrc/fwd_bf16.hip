@@ -289,7 +289,7 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
       if (lane == 0) sCount = count;
     }
     __syncthreads();
-    n_live_keys = sCount * p.block_k;
+    n_live_keys = __builtin_amdgcn_readfirstlane(sCount * p.block_k);
   }
   const int n_keys = BLOCK ? n_live_keys : kv_end;
   const int n_tiles = (n_keys + BK - 1) / BK;
@@ -314,6 +314,7 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
       }
       wave_lds_sync();
     }
+    wave_uniform = __builtin_amdgcn_readfirstlane((int)wave_uniform) != 0;
   }
 
   // ---- fixed-max bound of this lane's row, from the key blocks the row can
@@ -472,6 +473,27 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
   // BLOCK: one resource over all Nk rows, rows gathered by key index
   const DmaRsrc rk_all = dma_rsrc(kg, span(p.Nk, p.k_ss));
   const DmaRsrc rv_all = dma_rsrc(vg, span(p.Nk, p.v_ss));
+  // BLOCK: where this lane's row of load instruction j falls in the live-key
+  // list for the next tile to be issued: live block lb_blk[j], row lb_off[j]
+  // within it, and that block's id lb_id[j] (read from the list one tile
+  // ahead, so the lookup's latency is off the load issue). Tiles are
+  // issued in order, one list position BK further each time.
+  constexpr int NJB = BLOCK ? NIW : 1;
+  int lb_blk[NJB], lb_off[NJB], lb_id[NJB];
+  uint32_t lb_ks[NJB], lb_vs[NJB];  // swizzled chunk offsets (bytes) of the row's slot
+  int n_live_blocks = 0;
+  if constexpr (BLOCK) {
+    n_live_blocks = n_live_keys / p.block_k;
+#pragma unroll
+    for (int j = 0; j < NIW; ++j) {
+      const int r = dma_row0 + j * RPI;
+      lb_blk[j] = r / p.block_k;
+      lb_off[j] = r - lb_blk[j] * p.block_k;
+      lb_id[j] = sLive[min(lb_blk[j], max(n_live_blocks - 1, 0))];
+      lb_ks[j] = (uint32_t)(kswz<D>(r, dma_slot) * 16);
+      lb_vs[j] = (uint32_t)(vswz<D>(r, dma_slot) * 16);
+    }
+  }
   // step st loads tiles st * KS + k, k < KS (tiles past the end read as
   // zeros: their range is empty)
   auto issue_tile = [&](int st, auto bufc) {
@@ -502,14 +524,23 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
         const int L = t * BK + r;
         uint32_t ko = kOutOfRange, vo = kOutOfRange;
         if (L < n_live_keys) {
-          const int blk = L / p.block_k;
-          const int key = (int)sLive[blk] * p.block_k + (L - blk * p.block_k);
-          ko = (uint32_t)(key * p.k_ss + kswz<D>(r, dma_slot) * 8) * 2u;
-          vo = (uint32_t)(key * p.v_ss + vswz<D>(r, dma_slot) * 8) * 2u;
+          const int key = (int)__umul24(lb_id[j], p.block_k) + lb_off[j];
+          ko = (uint32_t)(key * p.k_ss) * 2u + lb_ks[j];
+          vo = (uint32_t)(key * p.v_ss) * 2u + lb_vs[j];
         }
         const int lds_row = (wave * NIW + j) * RPI;
         buf_load_lds16(rk_all, dk + lds_row * D, ko);
         buf_load_lds16(rv_all, dv + lds_row * D, vo);
+        // the same row of the next tile: BK list positions on (block_k >= 16,
+        // so at most four blocks further)
+        const int off = lb_off[j] + BK;
+        const int bk = p.block_k;
+        const int q = (off >= bk) + (off >= 2 * bk) + (off >= 3 * bk) + (off >= 4 * bk);
+        lb_off[j] = off - q * bk;
+        lb_blk[j] += q;
+        // the block's id for the next tile, read now and used one tile later
+        // (clamped: past the list's end the row is out of range anyway)
+        lb_id[j] = sLive[min(lb_blk[j], max(n_live_blocks - 1, 0))];
       }
     }
   };
@@ -564,21 +595,30 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
       }
       if (state == 1 && tile_k0 + BK > p.Nk) state = 2;
     } else {
-      // 16-key groups live for the wave (the same for every lane)
-      bool any = false, all = true;
+      // 16-key groups live for the wave (the same for every lane). A wave
+      // whose block row sees the whole union has only the list's tail to
+      // mask (tile_k0 < n_keys here).
+      if (wave_uniform) {
+        const int nl = n_live_keys - tile_k0;
 #pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        const int L = tile_k0 + 16 * gi;
-        bool live = L < n_live_keys;
-        if (live && !wave_uniform) {
-          const int j = L / p.block_k;
-          live = (bits[j >> 5] >> (j & 31)) & 1u;
+        for (int gi = 0; gi < 4; ++gi) grp_live[gi] = 16 * gi < nl;
+        state = (nl >= BK && !CAUSAL) ? 1 : 2;
+      } else {
+        bool any = false, all = true;
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          const int L = tile_k0 + 16 * gi;
+          bool live = L < n_live_keys;
+          if (live) {
+            const int j = L / p.block_k;
+            live = (bits[j >> 5] >> (j & 31)) & 1u;
+          }
+          grp_live[gi] = live;
+          any |= live;
+          all &= live;
         }
-        grp_live[gi] = live;
-        any |= live;
-        all &= live;
+        state = !any ? 0 : (all && !CAUSAL) ? 1 : 2;
       }
-      state = !any ? 0 : (all && !CAUSAL) ? 1 : 2;
     }
 
     // ---- S^T = K Q^T for the tile's two 32-key blocks (generic path)
