@@ -344,7 +344,7 @@ def main():
             p.call()
         e1.record()
         torch.cuda.synchronize()
-        b2b[p.name] = e0.elapsed_time(e1) / max(args.back_to_back, 1)
+        b2b[p.name] = e0.elapsed_time(e1) / args.back_to_back if args.back_to_back > 0 else None
         if probe is not None:
             live_clock = clk_mod.summary(probe.result())
             live_clock.update(window_ms=window_s * 1e3, calls=args.back_to_back,
