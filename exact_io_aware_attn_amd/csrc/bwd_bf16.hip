@@ -1065,11 +1065,21 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
   const __bf16* vg = (const __bf16*)p.v + b * p.v_sb + hkv * p.v_sh;
   const int dma_row0 = wave * NIW * RPI + lane / CH;
   const int dma_slot = lane % CH;
-  uint32_t ko[NIW], vo[NIW];
+  // byte offsets of this lane's chunk in the tile rows of load j. The K rows'
+  // swizzle depends on the row only through r % 4 (d = 128) or bit 1 of r
+  // (d = 64), the same for rows RPI apart, so the rows of different j differ
+  // by whole rows and only j = 0 is kept (fewer live registers through the
+  // tile loop).
+  static_assert(RPI % 4 == 0, "K row swizzle period");
+  uint32_t ko0, vo[NIW];
+  {
+    const int r = dma_row0;
+    ko0 = (uint32_t)(r * p.k_ss + vswz<D>(r, dma_slot) * 8) * 2u;
+  }
+  const uint32_t kstep = (uint32_t)(RPI * p.k_ss) * 2u;
 #pragma unroll
   for (int j = 0; j < NIW; ++j) {
     const int r = dma_row0 + j * RPI;
-    ko[j] = (uint32_t)(r * p.k_ss + vswz<D>(r, dma_slot) * 8) * 2u;
     vo[j] = (uint32_t)(r * p.v_ss + kswz<D>(r, dma_slot) * 8) * 2u;
   }
   auto issue = [&](int t, int buf) {
@@ -1080,7 +1090,7 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int j = 0; j < NIW; ++j) {
       const int lds_row = (wave * NIW + j) * RPI;
-      buf_load_lds16(rk, sK[buf] + lds_row * D, ko[j]);
+      buf_load_lds16(rk, sK[buf] + lds_row * D, ko0 + j * kstep);
       buf_load_lds16(rv, sV[buf] + lds_row * D, vo[j]);
     }
   };
@@ -1090,6 +1100,13 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+  // d = 128: byte offsets (within a tile) of the K-row fragments of k-steps
+  // 0, 2, 4, 6 (the fixed-order tile below)
+  int kofs[4] = {0, 0, 0, 0};
+  if constexpr (D == 128) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) kofs[m] = (qc * D + vswz<D>(qc, 4 * m + h) * 8) * 2;
+  }
   const float c = p.scale_log2;
   const int tr_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int tr_ch = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
@@ -1109,7 +1126,12 @@ __global__ void __launch_bounds__(64 * NW, 2) bwd_dq_kernel(const BwdParams p) {
   auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
   auto fast = [&](const __bf16* sk, const __bf16* sv) __attribute__((always_inline)) {
     auto sc_op = [&](int kb, int i) __attribute__((always_inline)) {
-      return (i & 1) ? row_frag<D, SW_K>(sv, kb, i >> 1, qc, h) : row_frag<D, SW_V>(sk, kb, i >> 1, qc, h);
+      if (i & 1) return row_frag<D, SW_K>(sv, kb, i >> 1, qc, h);
+      // K rows (vswz, d = 128): chunk 2ks + h of row 32 kb + qc sits at the
+      // slot of chunk 4 (ks / 2) + h plus 2 for odd ks, 32 rows further per
+      // block: four lane offsets and immediates
+      const int ks = i >> 1;
+      return *(const bf16x8*)((const char*)sk + kofs[ks >> 1] + 32 * (ks & 1) + kb * (64 * D));
     };
     // gradient product i of block kb: step u = 2 kb + i / MB, column block i % MB
     auto gr_op = [&](int kb, int i) __attribute__((always_inline)) {
