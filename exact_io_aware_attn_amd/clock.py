@@ -41,7 +41,8 @@ class ClockProbe:
     def start(self, window_s, warm_s=0.0, stream=None):
         import torch
         stream = stream if stream is not None else torch.cuda.current_stream()
-        self.out.zero_()
+        with torch.cuda.stream(stream):  # cleared in order with the probe's own writes
+            self.out.zero_()
         st = library().miclock_probe(
             ctypes.c_void_p(self.out.data_ptr()), self.n, int(warm_s * REALTIME_HZ),
             max(1, int(window_s * REALTIME_HZ)), ctypes.c_void_p(stream.cuda_stream))
