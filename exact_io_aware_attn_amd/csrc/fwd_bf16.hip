@@ -75,18 +75,25 @@ constexpr float kBlkSumMax = 4096.f;  // lazy rescale: a lane's 16-value block s
 // Hardware workgroup id -> (logical tile X, member g of the head group).
 // Groups of 8*G consecutive ids keep the G query heads of one KV head on one
 // XCD (ids are dealt round-robin over the 8 XCDs).
-__device__ __forceinline__ void map_workgroup(int i, int G, int nX, int& X, int& g) {
+// The id's divisions take the host's multiplier and shift (FwdParams::dv_*):
+// three scalar instructions each instead of an emulated integer division.
+__device__ __forceinline__ int fdiv(int n, uint32_t m, uint32_t s) {
+  return (int)((__umulhi((uint32_t)n, m) + (uint32_t)n) >> s);
+}
+__device__ __forceinline__ void map_workgroup(int i, const FwdParams& p, int nX, int& X, int& g) {
+  const int G = p.G;
   const int chunk = 8 * G;
   const int full = nX >> 3;
-  const int c = i / chunk;
+  const int c = fdiv(i, p.dv_8G_m, p.dv_8G_s);
   if (c < full) {
     const int r = i - c * chunk;
     X = c * 8 + (r & 7);
     g = r >> 3;
   } else {
     const int rr = i - full * chunk;
-    X = full * 8 + rr / G;
-    g = rr - (rr / G) * G;
+    const int qq = fdiv(rr, p.dv_G_m, p.dv_G_s);
+    X = full * 8 + qq;
+    g = rr - qq * G;
   }
 }
 
@@ -208,13 +215,13 @@ __global__ void __launch_bounds__(64 * NW, (D == 64 && NW == 4 && KS == 1) ? 3
   const int rw = wave % RW;  // 32-row block of this wave
   const int kp = wave / RW;  // key share of this wave (tiles t with t % KS == kp)
 
-  const int G = p.Hq / p.Hkv;
+  const int G = p.G;
   int X, g;
-  map_workgroup(blockIdx.x, G, p.n_qtiles * p.B * p.Hkv, X, g);
-  const int hkv = X % p.Hkv;
-  const int t2 = X / p.Hkv;
-  const int b = t2 % p.B;
-  const int qt_rank = t2 / p.B;
+  map_workgroup(blockIdx.x, p, p.n_qtiles * p.B * p.Hkv, X, g);
+  const int t2 = fdiv(X, p.dv_Hkv_m, p.dv_Hkv_s);
+  const int hkv = X - t2 * p.Hkv;
+  const int qt_rank = fdiv(t2, p.dv_B_m, p.dv_B_s);
+  const int b = t2 - qt_rank * p.B;
   const int qt = CAUSAL ? (p.n_qtiles - 1 - qt_rank) : qt_rank;
   const int hq = hkv * G + g;
   static_assert(!HP || (CAUSAL && !BLOCK && KS == 1), "priority boost: dense causal whole rows");
@@ -1055,6 +1062,20 @@ bool key_split(const FwdParams& p) {
   return !BLOCK && D == 64 && (p.Nk + BK - 1) / BK >= 4 && wg128 < 512;
 }
 
+// multiplier and shift of the division by d (1 <= d < 2^31) used in the kernel;
+// d = 0 (an empty problem, nothing launched) gives a harmless pair
+static void fast_div(uint32_t d, uint32_t& m, uint32_t& s) {
+  if (d == 0) {
+    m = 0;
+    s = 0;
+    return;
+  }
+  uint32_t sh = 0;
+  while ((1ull << sh) < d) ++sh;
+  s = sh;
+  m = (uint32_t)(((1ull << 32) * ((1ull << sh) - d)) / d + 1);
+}
+
 template <int D, bool CAUSAL, bool BLOCK, bool FX>
 hipError_t launch_one(const FwdParams& p0, hipStream_t s) {
   // 8 waves (256 rows) per workgroup share each K/V tile when that still
@@ -1064,6 +1085,11 @@ hipError_t launch_one(const FwdParams& p0, hipStream_t s) {
   // last rows need, which at d = 64 (three 4-wave workgroups per CU) costs
   // more than sharing each K/V tile among 8 waves saves
   FwdParams p = p0;
+  p.G = p.Hq / p.Hkv;
+  fast_div((uint32_t)p.G, p.dv_G_m, p.dv_G_s);
+  fast_div(8u * (uint32_t)p.G, p.dv_8G_m, p.dv_8G_s);
+  fast_div((uint32_t)p.Hkv, p.dv_Hkv_m, p.dv_Hkv_s);
+  fast_div((uint32_t)p.B, p.dv_B_m, p.dv_B_s);
   const int64_t big = (int64_t)((p.Nq + 255) / 256) * p.B * p.Hq;
   const bool wide = big >= 1024 && !(D == 64 && CAUSAL && !BLOCK);
   // rows are cut into 32-row segments of single block rows when block_q is

@@ -46,6 +46,10 @@ struct FwdParams {
   int fixed;          // 0 online, 1 fixed max, 2 fixed max with centred keys
   KStats ks;
   int n_qtiles;
+  // q = n / d as (umulhi(n, m) + n) >> s for 0 <= n < 2^31 (division by an
+  // invariant integer through a multiply, Granlund and Montgomery 1994)
+  uint32_t dv_G_m, dv_G_s, dv_8G_m, dv_8G_s, dv_Hkv_m, dv_Hkv_s, dv_B_m, dv_B_s;
+  int G;
 };
 
 struct KStatParams {
